@@ -1,0 +1,301 @@
+// cbs_api.cpp -- the C ABI declared in include/conv_bn_silu.h: handles,
+// host-side validation, variant dispatch and kernel launch.
+//
+// Nothing here touches device memory; every argument is checked before the
+// first HIP call, and every failure is reported as a status code.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <set>
+
+#include "../../include/conv_bn_silu.h"
+#include "cbs_launch.h"
+#include "cbs_shape.h"
+
+struct conv_bn_silu_handle {
+    int device;
+    int num_cu;
+    std::atomic<int> last_hip_error;
+};
+
+namespace {
+
+std::mutex g_handles_mu;
+std::set<const conv_bn_silu_handle *> g_handles;  // live handles; never dereference a foreign pointer
+
+bool handle_live(const conv_bn_silu_handle *h) {
+    std::lock_guard<std::mutex> lk(g_handles_mu);
+    return h != nullptr && g_handles.count(h) != 0;
+}
+
+// Geometry and overflow checks; fills `s` on success.
+int check_shape(int N, int C_in, int H, int W, int C_out, int KH, int KW, int stride, int pad,
+                int dtype, cbs::Shape *s) {
+    if (dtype != CBS_DTYPE_F32 && dtype != CBS_DTYPE_BF16) return CBS_ERR_INVALID_ARG;
+    if (N < 0 || C_in < 1 || H < 1 || W < 1 || C_out < 1 || KH < 1 || KW < 1 || stride < 1 || pad < 0)
+        return CBS_ERR_INVALID_ARG;
+    const int64_t span_h = (int64_t)H + 2 * (int64_t)pad - KH;
+    const int64_t span_w = (int64_t)W + 2 * (int64_t)pad - KW;
+    if (span_h < 0 || span_w < 0) return CBS_ERR_INVALID_ARG;  // the window does not fit
+    const int64_t OH = span_h / stride + 1, OW = span_w / stride + 1;
+    const int64_t lim = INT32_MAX;
+    const int64_t x_el = (int64_t)N * C_in * H * W;
+    const int64_t w_el = (int64_t)C_out * C_in * KH * KW;
+    const int64_t y_el = (int64_t)N * C_out * OH * OW;
+    // 32-bit index arithmetic inside the kernels must be exact, including the
+    // padded coordinates oh*stride - pad + kh.
+    if (x_el > lim || w_el > lim || y_el > lim || (int64_t)H + 2 * (int64_t)pad > lim ||
+        (int64_t)W + 2 * (int64_t)pad > lim || (int64_t)H * W > lim || (int64_t)N * OH * OW > lim)
+        return CBS_ERR_UNSUPPORTED;
+    s->N = N; s->C_in = C_in; s->H = H; s->W = W; s->C_out = C_out;
+    s->KH = KH; s->KW = KW; s->stride = stride; s->pad = pad;
+    s->OH = (int)OH; s->OW = (int)OW;
+    s->M = (int)(N * OH * OW);
+    s->K = C_in * KH * KW;
+    s->HW = H * W;
+    s->OHW = (int)(OH * OW);
+    s->T = KH * KW;
+    return CBS_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_pointers(const void *x, const void *w, const float *scale, const float *bias, const void *y,
+                   const cbs::Shape &s, int dtype) {
+    if (!x || !w || !scale || !bias || !y) return CBS_ERR_INVALID_ARG;
+    const uintptr_t e = dtype == CBS_DTYPE_BF16 ? 2 : 4;
+    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) % e != 0) return CBS_ERR_INVALID_ARG;
+    if (((uintptr_t)scale | (uintptr_t)bias) % 4 != 0) return CBS_ERR_INVALID_ARG;
+    const Range rx{(uintptr_t)x, (uintptr_t)x + (uintptr_t)s.N * s.C_in * s.HW * e};
+    const Range rw{(uintptr_t)w, (uintptr_t)w + (uintptr_t)s.C_out * s.K * e};
+    const Range rs{(uintptr_t)scale, (uintptr_t)scale + (uintptr_t)s.C_out * 4};
+    const Range rb{(uintptr_t)bias, (uintptr_t)bias + (uintptr_t)s.C_out * 4};
+    const Range ry{(uintptr_t)y, (uintptr_t)y + (uintptr_t)s.N * s.C_out * s.OHW * e};
+    if (overlap(ry, rx) || overlap(ry, rw) || overlap(ry, rs) || overlap(ry, rb)) return CBS_ERR_INVALID_ARG;
+    return CBS_OK;
+}
+
+int validate_all(const void *x, const void *w, const float *scale, const float *bias, const void *y, int N,
+                 int C_in, int H, int W, int C_out, int KH, int KW, int stride, int pad, int dtype,
+                 cbs::Shape *s) {
+    const int rc = check_shape(N, C_in, H, W, C_out, KH, KW, stride, pad, dtype, s);
+    if (rc != CBS_OK) return rc;
+    if (N == 0) return CBS_OK;  // nothing to do; pointers are not looked at
+    return check_pointers(x, w, scale, bias, y, *s, dtype);
+}
+
+bool variant_ok(int variant, const cbs::Shape &s, int dtype) {
+    switch (variant) {
+        case CBS_VARIANT_GEMM_GATHER: return cbs::gemm_gather_supports(s, dtype);
+        case CBS_VARIANT_SCALAR: return cbs::scalar_supports(s, dtype);
+        default: return false;
+    }
+}
+
+// AUTO dispatch.  Shape rules in the spirit of the page's hand-picked
+// thresholds ("Three kernels for one operation"): a specialised kernel where
+// the shape fits it, the scalar kernel for tiny problems where any setup
+// costs more than the work, otherwise the generic implicit GEMM.
+int select(const cbs::Shape &s, int dtype, int num_cu) {
+    (void)num_cu;
+    const int64_t macs = (int64_t)s.M * s.C_out * s.K;
+    if (macs <= (int64_t)1 << 21 && variant_ok(CBS_VARIANT_SCALAR, s, dtype)) return CBS_VARIANT_SCALAR;
+    return CBS_VARIANT_GEMM_GATHER;
+}
+
+hipError_t launch(int variant, const cbs::Shape &s, int dtype, int epi, const void *x, const void *w,
+                  const float *scale, const float *bias, void *y, hipStream_t st) {
+    switch (variant) {
+        case CBS_VARIANT_GEMM_GATHER: return cbs::launch_gemm_gather(s, dtype, epi, x, w, scale, bias, y, st);
+        case CBS_VARIANT_SCALAR: return cbs::launch_scalar(s, dtype, epi, x, w, scale, bias, y, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+int record_hip(conv_bn_silu_handle *h, hipError_t e) {
+    if (e == hipSuccess) return CBS_OK;
+    h->last_hip_error.store((int)e);
+    return CBS_ERR_HIP;
+}
+
+// Common front half of the run entry points: handle, arguments, device.
+int prologue(conv_bn_silu_t h, const void *x, const void *w, const float *scale, const float *bias,
+             const void *y, int N, int C_in, int H, int W, int C_out, int KH, int KW, int stride, int pad,
+             int dtype, cbs::Shape *s) {
+    if (!handle_live(h)) return CBS_ERR_BAD_HANDLE;
+    const int rc = validate_all(x, w, scale, bias, y, N, C_in, H, W, C_out, KH, KW, stride, pad, dtype, s);
+    if (rc != CBS_OK) return rc;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return CBS_ERR_NO_DEVICE;
+    if (dev != h->device) return CBS_ERR_INVALID_ARG;  // the handle belongs to another device
+    return CBS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int conv_bn_silu_create(conv_bn_silu_t *out_handle) {
+    if (!out_handle) return CBS_ERR_INVALID_ARG;
+    *out_handle = nullptr;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count < 1) return CBS_ERR_NO_DEVICE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CBS_ERR_NO_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return CBS_ERR_NO_DEVICE;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return CBS_ERR_UNSUPPORTED;
+    auto *h = new conv_bn_silu_handle;
+    h->device = dev;
+    h->num_cu = prop.multiProcessorCount;
+    h->last_hip_error.store(0);
+    {
+        std::lock_guard<std::mutex> lk(g_handles_mu);
+        g_handles.insert(h);
+    }
+    *out_handle = h;
+    return CBS_OK;
+}
+
+int conv_bn_silu_destroy(conv_bn_silu_t h) {
+    if (!h) return CBS_OK;
+    {
+        std::lock_guard<std::mutex> lk(g_handles_mu);
+        if (g_handles.erase(h) == 0) return CBS_ERR_BAD_HANDLE;
+    }
+    delete h;
+    return CBS_OK;
+}
+
+int conv_bn_silu_run_variant(conv_bn_silu_t h, int variant, const void *x, const void *w, const float *scale,
+                             const float *bias, void *y, int N, int C_in, int H, int W, int C_out, int KH, int KW,
+                             int stride, int pad, int dtype, void *stream) {
+    if (variant < 0 || variant >= CBS_VARIANT_COUNT_) return CBS_ERR_INVALID_ARG;
+    cbs::Shape s;
+    int rc = prologue(h, x, w, scale, bias, y, N, C_in, H, W, C_out, KH, KW, stride, pad, dtype, &s);
+    if (rc != CBS_OK) return rc;
+    if (variant == CBS_VARIANT_AUTO) variant = select(s, dtype, h->num_cu);
+    else if (!variant_ok(variant, s, dtype)) return CBS_ERR_UNSUPPORTED;
+    if (s.N == 0) return CBS_OK;
+    return record_hip(h, launch(variant, s, dtype, cbs::kFused, x, w, scale, bias, y, (hipStream_t)stream));
+}
+
+int conv_bn_silu_run(conv_bn_silu_t h, const void *x, const void *w, const float *scale, const float *bias,
+                     void *y, int N, int C_in, int H, int W, int C_out, int KH, int KW, int stride, int pad,
+                     int dtype, void *stream) {
+    return conv_bn_silu_run_variant(h, CBS_VARIANT_AUTO, x, w, scale, bias, y, N, C_in, H, W, C_out, KH, KW,
+                                    stride, pad, dtype, stream);
+}
+
+int conv_bn_silu_run_unfused(conv_bn_silu_t h, const void *x, const void *w, const float *scale,
+                             const float *bias, void *t1, void *t2, void *y, int N, int C_in, int H, int W,
+                             int C_out, int KH, int KW, int stride, int pad, int dtype, void *stream) {
+    cbs::Shape s;
+    int rc = prologue(h, x, w, scale, bias, y, N, C_in, H, W, C_out, KH, KW, stride, pad, dtype, &s);
+    if (rc != CBS_OK) return rc;
+    if (s.N == 0) return CBS_OK;
+    const uintptr_t e = dtype == CBS_DTYPE_BF16 ? 2 : 4;
+    if (!t1 || !t2 || ((uintptr_t)t1 | (uintptr_t)t2) % e != 0) return CBS_ERR_INVALID_ARG;
+    const uintptr_t ybytes = (uintptr_t)s.N * s.C_out * s.OHW * e;
+    const Range r1{(uintptr_t)t1, (uintptr_t)t1 + ybytes}, r2{(uintptr_t)t2, (uintptr_t)t2 + ybytes};
+    const Range others[] = {{(uintptr_t)x, (uintptr_t)x + (uintptr_t)s.N * s.C_in * s.HW * e},
+                            {(uintptr_t)w, (uintptr_t)w + (uintptr_t)s.C_out * s.K * e},
+                            {(uintptr_t)scale, (uintptr_t)scale + (uintptr_t)s.C_out * 4},
+                            {(uintptr_t)bias, (uintptr_t)bias + (uintptr_t)s.C_out * 4},
+                            {(uintptr_t)y, (uintptr_t)y + ybytes}};
+    if (overlap(r1, r2)) return CBS_ERR_INVALID_ARG;
+    for (const Range &o : others)
+        if (overlap(r1, o) || overlap(r2, o)) return CBS_ERR_INVALID_ARG;
+    const hipStream_t st = (hipStream_t)stream;
+    const int variant = select(s, dtype, h->num_cu);
+    rc = record_hip(h, launch(variant, s, dtype, cbs::kConvOnly, x, w, scale, bias, t1, st));
+    if (rc != CBS_OK) return rc;
+    rc = record_hip(h, cbs::launch_bn_pass(s, dtype, t1, scale, bias, t2, st));
+    if (rc != CBS_OK) return rc;
+    return record_hip(h, cbs::launch_silu_pass(s, dtype, t2, y, st));
+}
+
+int conv_bn_silu_output_hw(int H, int W, int KH, int KW, int stride, int pad, int *OH, int *OW) {
+    if (!OH || !OW) return CBS_ERR_INVALID_ARG;
+    cbs::Shape s;
+    const int rc = check_shape(1, 1, H, W, 1, KH, KW, stride, pad, CBS_DTYPE_F32, &s);
+    if (rc != CBS_OK) return rc;
+    *OH = s.OH;
+    *OW = s.OW;
+    return CBS_OK;
+}
+
+int conv_bn_silu_validate(const void *x, const void *w, const float *scale, const float *bias, const void *y,
+                          int N, int C_in, int H, int W, int C_out, int KH, int KW, int stride, int pad,
+                          int dtype) {
+    cbs::Shape s;
+    return validate_all(x, w, scale, bias, y, N, C_in, H, W, C_out, KH, KW, stride, pad, dtype, &s);
+}
+
+int conv_bn_silu_select_variant(int N, int C_in, int H, int W, int C_out, int KH, int KW, int stride, int pad,
+                                int dtype, int num_cu) {
+    cbs::Shape s;
+    if (check_shape(N, C_in, H, W, C_out, KH, KW, stride, pad, dtype, &s) != CBS_OK) return -1;
+    return select(s, dtype, num_cu);
+}
+
+int conv_bn_silu_variant_supports(int variant, int N, int C_in, int H, int W, int C_out, int KH, int KW,
+                                  int stride, int pad, int dtype) {
+    cbs::Shape s;
+    if (check_shape(N, C_in, H, W, C_out, KH, KW, stride, pad, dtype, &s) != CBS_OK) return 0;
+    if (variant == CBS_VARIANT_AUTO) return 1;
+    return variant_ok(variant, s, dtype) ? 1 : 0;
+}
+
+const char *conv_bn_silu_status_string(int status) {
+    switch (status) {
+        case CBS_OK: return "ok";
+        case CBS_ERR_INVALID_ARG: return "invalid argument";
+        case CBS_ERR_UNSUPPORTED: return "unsupported (device, size or variant)";
+        case CBS_ERR_NO_DEVICE: return "no HIP device";
+        case CBS_ERR_HIP: return "HIP runtime error";
+        case CBS_ERR_BAD_HANDLE: return "bad handle";
+        default: return "unknown";
+    }
+}
+
+const char *conv_bn_silu_variant_name(int variant) {
+    switch (variant) {
+        case CBS_VARIANT_AUTO: return "auto";
+        case CBS_VARIANT_GEMM_GATHER: return "gemm_gather";
+        case CBS_VARIANT_GEMM_WINDOW: return "gemm_window";
+        case CBS_VARIANT_POINTWISE: return "pointwise";
+        case CBS_VARIANT_SMALL_K: return "small_k";
+        case CBS_VARIANT_SCALAR: return "scalar";
+        default: return "unknown";
+    }
+}
+
+int conv_bn_silu_last_hip_error(conv_bn_silu_t h) {
+    if (!handle_live(h)) return 0;
+    return h->last_hip_error.load();
+}
+
+int conv_bn_silu_fold_bn(const float *gamma, const float *beta, const float *mean, const float *var, float eps,
+                         const float *conv_bias, int C_out, float *scale, float *bias) {
+    if (!gamma || !beta || !mean || !var || !scale || !bias || C_out < 1 || !(eps >= 0.f))
+        return CBS_ERR_INVALID_ARG;
+    for (int c = 0; c < C_out; ++c)
+        if (!((double)var[c] + (double)eps > 0.0)) return CBS_ERR_INVALID_ARG;
+    for (int c = 0; c < C_out; ++c) {
+        const double sc = (double)gamma[c] / std::sqrt((double)var[c] + (double)eps);
+        const double cb = conv_bias ? (double)conv_bias[c] : 0.0;
+        scale[c] = (float)sc;
+        bias[c] = (float)((double)beta[c] + (cb - (double)mean[c]) * sc);
+    }
+    return CBS_OK;
+}
+
+}  // extern "C"

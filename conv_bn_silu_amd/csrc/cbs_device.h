@@ -1,0 +1,56 @@
+// cbs_device.h -- device-side helpers shared by the gfx950 kernels: element
+// types, the fused epilogue, MFMA fragment types and the geometry record.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cbs_shape.h"
+
+namespace cbs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Epilogue of "Fusing an Epilogue" (section "The shape of it"): the folded
+// batch norm is a multiply and an add with the output channel's parameters,
+// then SiLU(v) = v * sigmoid(v), sigmoid(v) = 1 / (1 + e^-v).  e^-v is taken
+// as 2^(-v*log2 e) on the hardware exp2 unit and the quotient through the
+// hardware reciprocal (both about 1 ulp in fp32).  For v below about -88,
+// e^-v overflows to +inf, the reciprocal gives 0 and the result is -0, the
+// correct limit; for large v the result tends to v.
+__device__ __forceinline__ float bn_silu(float acc, float scale, float bias) {
+    float v = __builtin_fmaf(acc, scale, bias);
+    float e = __builtin_amdgcn_exp2f(v * -1.4426950408889634f);
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Round to bfloat16, nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ static __forceinline__ float load(const float *p) { return *p; }
+    __device__ static __forceinline__ void store(float *p, float v) { *p = v; }
+};
+template <> struct Elem<uint16_t> {
+    __device__ static __forceinline__ float load(const uint16_t *p) { return bf16_to_f32(*p); }
+    __device__ static __forceinline__ void store(uint16_t *p, float v) { *p = to_bf16(v); }
+};
+
+}  // namespace cbs

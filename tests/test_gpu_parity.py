@@ -1,0 +1,183 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the fp64
+CPU oracle on the same seeded inputs, element by element, under the stated
+tolerances (fp32: |err| <= 1e-4*(1+|ref|); bf16: |err| <= 1.6e-2*|ref| + 1e-3).
+
+Coverage: every variant on every shape of a sweep of small and ragged
+geometries (odd sizes, kernel sizes 1-7, strides 1-3, padding 0-3, channel
+counts off the tile sizes, M and K tails); the five workloads with a reduced
+batch checked in full; the five workloads at full size, in the launch
+configuration the benchmark times, on sampled outputs; and the degenerate
+cases (empty batch, 1x1x1, padding wider than the window's reach)."""
+import numpy as np
+import pytest
+
+from conv_bn_silu_amd import synth
+import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = synth.DTYPE_F32, synth.DTYPE_BF16
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from conv_bn_silu_amd import binding
+    return binding
+
+
+def run(B, inp, variant="auto", stride=None):
+    import torch
+    x, w, sc, bi = U.upload(inp)
+    y = B.conv_bn_silu(x, w, sc, bi, stride=inp.wl.stride, pad=inp.wl.pad, variant=variant)
+    torch.cuda.synchronize()
+    return y
+
+
+SWEEP = [
+    # N, C_in, H, W, C_out, KH, KW, stride, pad
+    (1, 3, 7, 9, 5, 3, 3, 1, 1),
+    (2, 16, 13, 11, 33, 3, 3, 2, 1),
+    (1, 8, 5, 5, 17, 5, 5, 1, 2),
+    (3, 5, 9, 10, 7, 7, 7, 3, 3),
+    (2, 32, 17, 17, 48, 1, 1, 1, 0),
+    (1, 40, 10, 12, 70, 1, 1, 2, 0),
+    (2, 3, 33, 31, 16, 3, 3, 2, 1),
+    (1, 64, 9, 9, 130, 3, 3, 1, 1),
+    (2, 72, 6, 7, 64, 3, 3, 1, 0),
+    (1, 1, 1, 1, 1, 1, 1, 1, 0),
+    (1, 2, 3, 3, 3, 3, 3, 1, 3),
+    (1, 4, 4, 6, 2, 2, 3, 2, 0),
+    (2, 512, 4, 4, 40, 3, 3, 1, 1),
+    (1, 256, 20, 20, 256, 1, 1, 1, 0),
+    (2, 24, 21, 19, 144, 3, 3, 1, 1),
+    (1, 3, 64, 64, 16, 3, 3, 2, 1),
+    (2, 96, 12, 12, 64, 3, 3, 2, 1),
+]
+
+
+def sweep_cases():
+    from conv_bn_silu_amd import binding as B
+    out = []
+    for i, (N, C_in, H, W, C_out, KH, KW, s, p) in enumerate(SWEEP):
+        for dt in (F32, BF16):
+            for vname, v in B.VARIANTS.items():
+                if v == 0 or not B.variant_supports(v, N, C_in, H, W, C_out, KH, KW, s, p, dt):
+                    continue
+                out.append(pytest.param(i, dt, vname, id=f"s{i}-{'bf16' if dt else 'f32'}-{vname}"))
+            out.append(pytest.param(i, dt, "auto", id=f"s{i}-{'bf16' if dt else 'f32'}-auto"))
+    return out
+
+
+@pytest.mark.parametrize("case,dt,variant", sweep_cases())
+def test_sweep(lib, case, dt, variant):
+    N, C_in, H, W, C_out, KH, KW, s, p = SWEEP[case]
+    wl = synth.Workload(f"sweep{case}", dt, N, C_in, H, W, C_out, KH, KW, s, p, "n01", 2000 + case)
+    inp = synth.make_inputs(wl)
+    U.say(f"[sweep] case {case} {SWEEP[case]} dtype {dt} variant {variant}")
+    y = run(lib, inp, variant)
+    U.check(U.to_f64(y), U.oracle_full(inp), dt, f"sweep{case}/{variant}")
+
+
+REDUCED = {"c1": {}, "c2": {"N": 1}, "c3": {"N": 1, "H": 96, "W": 80}, "c4": {"N": 1, "H": 130, "W": 98},
+           "c5": {"N": 3}}
+
+
+def workload_variants(key, reduced=True):
+    from conv_bn_silu_amd import binding as B
+    wl = synth.WORKLOADS[key].with_(**REDUCED[key]) if reduced else synth.WORKLOADS[key]
+    vs = ["auto"] + [n for n, v in B.VARIANTS.items()
+                     if v and B.variant_supports(v, wl.N, wl.C_in, wl.H, wl.W, wl.C_out, wl.KH, wl.KW,
+                                                 wl.stride, wl.pad, wl.dtype)]
+    return [pytest.param(key, v, id=f"{key}-{v}") for v in vs]
+
+
+@pytest.mark.parametrize("key,variant", [p for k in sorted(REDUCED) for p in workload_variants(k)])
+def test_workload_reduced_full_check(lib, key, variant):
+    """Each workload's layer at a reduced batch/size (several tiles, ragged
+    tails), every output checked against the full oracle."""
+    wl = synth.WORKLOADS[key].with_(**REDUCED[key])
+    inp = synth.make_inputs(wl)
+    U.say(f"[reduced] {key} {wl} variant {variant}")
+    y = run(lib, inp, variant)
+    U.check(U.to_f64(y), U.oracle_full(inp), wl.dtype, f"{key}/{variant}")
+
+
+@pytest.mark.parametrize("key", sorted(synth.WORKLOADS))
+def test_workload_full_size_sampled(lib, key):
+    """Full-size workload through AUTO dispatch (what the benchmark times):
+    sampled outputs against the oracle, every output finite."""
+    wl = synth.WORKLOADS[key]
+    inp = synth.make_inputs(wl)
+    U.say(f"[full] {key} {wl.name}")
+    y = U.to_f64(run(lib, inp)).ravel()
+    assert np.isfinite(y).all()
+    idx = U.sample_indices(wl, 6000, seed=wl.seed)
+    U.check(y[idx], U.oracle_points(inp, idx), wl.dtype, f"{key}/full")
+
+
+def test_empty_batch_is_a_no_op(lib):
+    import torch
+    h = lib.default_library()
+    U.say("[edge] N=0")
+    h.run_ptr(0, 0, 0, 0, 0, 0, 0, 3, 8, 8, 4, 3, 3, 1, 1, lib.DTYPE_BF16,
+              torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+
+
+def test_deterministic_and_no_stray_writes(lib):
+    """Two runs give the same bits, and the guard bands around y stay intact."""
+    import torch
+    for key in ("c1", "c5"):
+        wl = synth.WORKLOADS[key].with_(**REDUCED[key])
+        inp = synth.make_inputs(wl)
+        x, w, sc, bi = U.upload(inp)
+        n_out = wl.N * wl.C_out * wl.OH * wl.OW
+        guard = 4096
+        dt = torch.bfloat16 if wl.dtype == BF16 else torch.float32
+        buf = torch.full((n_out + 2 * guard,), 12345.0, dtype=dt, device="cuda")
+        U.say(f"[guard] {key}")
+        outs = []
+        for _ in range(2):
+            y = buf[guard:guard + n_out].view(wl.N, wl.C_out, wl.OH, wl.OW)
+            lib.conv_bn_silu(x, w, sc, bi, stride=wl.stride, pad=wl.pad, out=y)
+            torch.cuda.synchronize()
+            outs.append(y.clone())
+        assert torch.equal(outs[0].view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                           outs[1].view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+        assert bool((buf[:guard] == 12345.0).all()) and bool((buf[guard + n_out:] == 12345.0).all())
+
+
+def test_side_stream(lib):
+    import torch
+    wl = synth.WORKLOADS["c5"].with_(N=2)
+    inp = synth.make_inputs(wl)
+    x, w, sc, bi = U.upload(inp)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    U.say("[stream] side stream")
+    with torch.cuda.stream(s):
+        y = lib.conv_bn_silu(x, w, sc, bi, stride=1, pad=1)
+    s.synchronize()
+    U.check(U.to_f64(y), U.oracle_full(inp), BF16, "side stream")
+
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3"])
+def test_unfused_sequence(lib, key):
+    """The three-kernel baseline: each pass checked against the oracle's pass
+    applied to the GPU's own input of that pass (so the bf16 rounding of the
+    stored intermediates does not enter the comparison)."""
+    import oracle
+    o = oracle.get()
+    wl = synth.WORKLOADS[key].with_(**REDUCED[key])
+    inp = synth.make_inputs(wl)
+    x, w, sc, bi = U.upload(inp)
+    U.say(f"[unfused] {key}")
+    y, t1, t2 = lib.conv_bn_silu_unfused(x, w, sc, bi, stride=wl.stride, pad=wl.pad)
+    import torch
+    torch.cuda.synchronize()
+    U.check(U.to_f64(t1), o.conv(inp.x, inp.w, wl.stride, wl.pad), wl.dtype, "conv pass")
+    t1h, t2h = U.to_f64(t1), U.to_f64(t2)
+    U.check(t2h, o.bn(t1h, inp.scale, inp.bias), wl.dtype, "bn pass")
+    U.check(U.to_f64(y), o.silu(t2h), wl.dtype, "silu pass")
