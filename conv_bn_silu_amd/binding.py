@@ -11,6 +11,12 @@ from __future__ import annotations
 import ctypes
 import os
 
+# torch must be imported before the library is loaded: torch ships its own
+# HIP runtime, and the library has to bind to that same runtime, or the
+# process would hold two HIP runtimes and torch's streams and allocations
+# would be foreign to the library's.
+import torch  # noqa: F401
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libconv_bn_silu.so")
 

@@ -20,6 +20,11 @@ struct conv_bn_silu_handle {
     int device;
     int num_cu;
     std::atomic<int> last_hip_error;
+    // Device workspace for packed weights, grown on demand and kept until
+    // the handle is destroyed.
+    std::mutex ws_mu;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
 };
 
 namespace {
@@ -94,8 +99,18 @@ int validate_all(const void *x, const void *w, const float *scale, const float *
 bool variant_ok(int variant, const cbs::Shape &s, int dtype) {
     switch (variant) {
         case CBS_VARIANT_GEMM_GATHER: return cbs::gemm_gather_supports(s, dtype);
+        case CBS_VARIANT_GEMM_WINDOW: return cbs::window_supports(s, dtype);
+        case CBS_VARIANT_POINTWISE: return cbs::pointwise_supports(s, dtype);
         case CBS_VARIANT_SCALAR: return cbs::scalar_supports(s, dtype);
         default: return false;
+    }
+}
+
+// Alignment the vectorised variants need beyond element alignment.
+bool pointers_ok(int variant, const void *x, const void *w, const void *y) {
+    switch (variant) {
+        case CBS_VARIANT_POINTWISE: return cbs::pointwise_pointers_ok(x, w, y);
+        default: return true;
     }
 }
 
@@ -107,13 +122,49 @@ int select(const cbs::Shape &s, int dtype, int num_cu) {
     (void)num_cu;
     const int64_t macs = (int64_t)s.M * s.C_out * s.K;
     if (macs <= (int64_t)1 << 21 && variant_ok(CBS_VARIANT_SCALAR, s, dtype)) return CBS_VARIANT_SCALAR;
+    if (variant_ok(CBS_VARIANT_POINTWISE, s, dtype)) return CBS_VARIANT_POINTWISE;
+    if (variant_ok(CBS_VARIANT_GEMM_WINDOW, s, dtype)) return CBS_VARIANT_GEMM_WINDOW;
     return CBS_VARIANT_GEMM_GATHER;
 }
 
+// AUTO dispatch at run time: the shape's choice, unless its pointers are not
+// aligned for it, in which case the generic kernel serves the call.
+int select_for_call(const cbs::Shape &s, int dtype, int num_cu, const void *x, const void *w, const void *y) {
+    const int v = select(s, dtype, num_cu);
+    return pointers_ok(v, x, w, y) ? v : CBS_VARIANT_GEMM_GATHER;
+}
+
+// Make the handle's workspace at least `bytes` long.  Growing it frees the
+// old buffer (which waits for the device) and allocates a new one.
+hipError_t ensure_workspace(conv_bn_silu_handle *h, size_t bytes, void **out) {
+    std::lock_guard<std::mutex> lk(h->ws_mu);
+    if (h->ws_bytes < bytes) {
+        if (h->ws) {
+            (void)hipFree(h->ws);
+            h->ws = nullptr;
+            h->ws_bytes = 0;
+        }
+        const size_t want = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
+        const hipError_t e = hipMalloc(&h->ws, want);
+        if (e != hipSuccess) return e;
+        h->ws_bytes = want;
+    }
+    *out = h->ws;
+    return hipSuccess;
+}
+
 hipError_t launch(int variant, const cbs::Shape &s, int dtype, int epi, const void *x, const void *w,
-                  const float *scale, const float *bias, void *y, hipStream_t st) {
+                  const float *scale, const float *bias, void *y, hipStream_t st, int num_cu,
+                  void *workspace) {
+    // hipGetLastError reports the last error of any HIP call on this thread;
+    // clear whatever an earlier, unrelated call left so that the launcher's
+    // check sees only its own launch.
+    (void)hipGetLastError();
     switch (variant) {
         case CBS_VARIANT_GEMM_GATHER: return cbs::launch_gemm_gather(s, dtype, epi, x, w, scale, bias, y, st);
+        case CBS_VARIANT_POINTWISE: return cbs::launch_pointwise(s, epi, x, w, scale, bias, y, st, num_cu);
+        case CBS_VARIANT_GEMM_WINDOW:
+            return cbs::launch_window(s, epi, x, w, scale, bias, y, workspace, st, num_cu);
         case CBS_VARIANT_SCALAR: return cbs::launch_scalar(s, dtype, epi, x, w, scale, bias, y, st);
         default: return hipErrorInvalidValue;
     }
@@ -149,7 +200,10 @@ int conv_bn_silu_create(conv_bn_silu_t *out_handle) {
     if (hipGetDeviceCount(&count) != hipSuccess || count < 1) return CBS_ERR_NO_DEVICE;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return CBS_ERR_NO_DEVICE;
-    hipDeviceProp_t prop;
+    // The property record is over-allocated: the process's HIP runtime may be
+    // a different release than the headers this file was compiled with.
+    alignas(64) static thread_local unsigned char prop_buf[sizeof(hipDeviceProp_t) + 8192];
+    hipDeviceProp_t &prop = *reinterpret_cast<hipDeviceProp_t *>(prop_buf);
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return CBS_ERR_NO_DEVICE;
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return CBS_ERR_UNSUPPORTED;
     auto *h = new conv_bn_silu_handle;
@@ -170,6 +224,7 @@ int conv_bn_silu_destroy(conv_bn_silu_t h) {
         std::lock_guard<std::mutex> lk(g_handles_mu);
         if (g_handles.erase(h) == 0) return CBS_ERR_BAD_HANDLE;
     }
+    if (h->ws) (void)hipFree(h->ws);
     delete h;
     return CBS_OK;
 }
@@ -181,10 +236,16 @@ int conv_bn_silu_run_variant(conv_bn_silu_t h, int variant, const void *x, const
     cbs::Shape s;
     int rc = prologue(h, x, w, scale, bias, y, N, C_in, H, W, C_out, KH, KW, stride, pad, dtype, &s);
     if (rc != CBS_OK) return rc;
-    if (variant == CBS_VARIANT_AUTO) variant = select(s, dtype, h->num_cu);
-    else if (!variant_ok(variant, s, dtype)) return CBS_ERR_UNSUPPORTED;
     if (s.N == 0) return CBS_OK;
-    return record_hip(h, launch(variant, s, dtype, cbs::kFused, x, w, scale, bias, y, (hipStream_t)stream));
+    if (variant == CBS_VARIANT_AUTO) variant = select_for_call(s, dtype, h->num_cu, x, w, y);
+    else if (!variant_ok(variant, s, dtype) || !pointers_ok(variant, x, w, y)) return CBS_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    if (variant == CBS_VARIANT_GEMM_WINDOW) {
+        rc = record_hip(h, ensure_workspace(h, cbs::window_workspace_bytes(s), &ws));
+        if (rc != CBS_OK) return rc;
+    }
+    return record_hip(h, launch(variant, s, dtype, cbs::kFused, x, w, scale, bias, y, (hipStream_t)stream,
+                                h->num_cu, ws));
 }
 
 int conv_bn_silu_run(conv_bn_silu_t h, const void *x, const void *w, const float *scale, const float *bias,
@@ -214,11 +275,18 @@ int conv_bn_silu_run_unfused(conv_bn_silu_t h, const void *x, const void *w, con
     for (const Range &o : others)
         if (overlap(r1, o) || overlap(r2, o)) return CBS_ERR_INVALID_ARG;
     const hipStream_t st = (hipStream_t)stream;
-    const int variant = select(s, dtype, h->num_cu);
-    rc = record_hip(h, launch(variant, s, dtype, cbs::kConvOnly, x, w, scale, bias, t1, st));
+    const int variant = select_for_call(s, dtype, h->num_cu, x, w, t1);
+    void *ws = nullptr;
+    if (variant == CBS_VARIANT_GEMM_WINDOW) {
+        rc = record_hip(h, ensure_workspace(h, cbs::window_workspace_bytes(s), &ws));
+        if (rc != CBS_OK) return rc;
+    }
+    rc = record_hip(h, launch(variant, s, dtype, cbs::kConvOnly, x, w, scale, bias, t1, st, h->num_cu, ws));
     if (rc != CBS_OK) return rc;
+    (void)hipGetLastError();
     rc = record_hip(h, cbs::launch_bn_pass(s, dtype, t1, scale, bias, t2, st));
     if (rc != CBS_OK) return rc;
+    (void)hipGetLastError();
     return record_hip(h, cbs::launch_silu_pass(s, dtype, t2, y, st));
 }
 

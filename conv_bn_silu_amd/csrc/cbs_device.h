@@ -43,6 +43,30 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
+// Raw buffer access.  A buffer resource carries the tensor's size in bytes;
+// a load at an offset past it returns zero and a store there is dropped, so
+// masked lanes need no branch (branches around memory operations make the
+// compiler wait for every outstanding access instead of just the ones a
+// value depends on).  Offsets are 32-bit, so tensors used this way must stay
+// below kMaxBufferBytes.
+constexpr uint32_t kOOB = 0xFFFFFFF0u;           // past the end of every buffer
+constexpr uint64_t kMaxBufferBytes = 0xFFFFFF00ull;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
     __device__ static __forceinline__ float load(const float *p) { return *p; }

@@ -18,6 +18,20 @@ bool gemm_gather_supports(const Shape &s, int dtype);
 hipError_t launch_gemm_gather(const Shape &s, int dtype, int epi, const void *x, const void *w,
                               const float *scale, const float *bias, void *y, hipStream_t st);
 
+// 1x1, stride 1, pad 0 streaming GEMM (bf16, C_in % 8 == 0, C_in <= 256,
+// H*W % 8 == 0); x, w and y 16-byte aligned.
+bool pointwise_supports(const Shape &s, int dtype);
+bool pointwise_pointers_ok(const void *x, const void *w, const void *y);
+hipError_t launch_pointwise(const Shape &s, int epi, const void *x, const void *w, const float *scale,
+                            const float *bias, void *y, hipStream_t st, int num_cu);
+
+// Window-staged implicit GEMM (bf16; W, OW multiples of 4).  Needs a
+// workspace of window_workspace_bytes() for the packed weights.
+bool window_supports(const Shape &s, int dtype);
+size_t window_workspace_bytes(const Shape &s);
+hipError_t launch_window(const Shape &s, int epi, const void *x, const void *w, const float *scale,
+                         const float *bias, void *y, void *workspace, hipStream_t st, int num_cu);
+
 // One output element per lane; any geometry, both dtypes.
 bool scalar_supports(const Shape &s, int dtype);
 hipError_t launch_scalar(const Shape &s, int dtype, int epi, const void *x, const void *w,

@@ -21,6 +21,17 @@ struct Shape {
     int T;    // KH * KW (kernel taps)
 };
 
+// Tiling of the window kernel: TH x TW output pixels per tile; the input
+// window of a tile is FR rows x FC columns, stored with row pitch FCP
+// records and, for stride > 1, columns grouped by residue (CS per group).
+struct WinGeo {
+    int TH, TW, FR, FC, CS, FCP;
+    int ncg;                           // staging column groups per window row
+    int tiles_h, tiles_w, co_tiles, n_tiles;
+    int n_chunks;                      // 32-channel blocks of C_in
+    int tiles_per_wg, n_wg;            // contiguous tile run per workgroup, workgroups
+};
+
 // Epilogue modes: the fused operator, or the plain convolution (the first
 // kernel of the unfused sequence).
 enum Epilogue { kFused = 0, kConvOnly = 1 };

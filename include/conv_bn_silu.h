@@ -77,7 +77,8 @@ enum {
 typedef struct conv_bn_silu_handle *conv_bn_silu_t;
 
 /* Create a handle bound to the current HIP device.  Queries the device once
- * (architecture, compute-unit count) for dispatch; allocates no device memory.
+ * (architecture, compute-unit count) for dispatch; allocates no device memory
+ * (the handle's workspace, see conv_bn_silu_run, is allocated on first use).
  * Returns CBS_ERR_NO_DEVICE without a visible device, CBS_ERR_UNSUPPORTED if
  * the device is not gfx950, CBS_ERR_INVALID_ARG if out_handle is NULL.
  * On failure *out_handle is set to NULL. */
@@ -91,8 +92,14 @@ int conv_bn_silu_destroy(conv_bn_silu_t handle);
  * every other size must be >= 1, stride >= 1, pad >= 0, and the output must be non-empty.
  * y must not overlap x, w, scale or bias (the convolution reads neighbours,
  * so in-place use is not possible).  x, w and y must be aligned to their
- * element size, scale and bias to 4 bytes.  A handle may be used from several
- * threads and streams at once: the call keeps no state on the device. */
+ * element size, scale and bias to 4 bytes.
+ * Workspace: variants that reorder the weights first (the window variant)
+ * keep the reordered copy in a device workspace owned by the handle.  The
+ * first call that needs a larger workspace than the handle holds allocates it
+ * (hipMalloc; growing it first frees the old one, which waits for the
+ * device); later calls allocate nothing.  Because calls share that
+ * workspace, calls made with one handle must not execute concurrently: use
+ * one handle per stream (or per thread) for concurrent work. */
 int conv_bn_silu_run(conv_bn_silu_t handle,
                      const void *x, const void *w, const float *scale, const float *bias,
                      void *y,

@@ -54,6 +54,13 @@ SWEEP = [
     (2, 24, 21, 19, 144, 3, 3, 1, 1),
     (1, 3, 64, 64, 16, 3, 3, 2, 1),
     (2, 96, 12, 12, 64, 3, 3, 2, 1),
+    # 1x1 shapes for the pointwise variant: K tail, channel tails, several
+    # channel tiles, tiny and many images
+    (3, 40, 4, 6, 70, 1, 1, 1, 0),
+    (2, 72, 8, 10, 300, 1, 1, 1, 0),
+    (5, 256, 8, 8, 16, 1, 1, 1, 0),
+    (1, 8, 1, 8, 1, 1, 1, 1, 0),
+    (7, 128, 12, 12, 200, 1, 1, 1, 0),
 ]
 
 
@@ -181,3 +188,23 @@ def test_unfused_sequence(lib, key):
     t1h, t2h = U.to_f64(t1), U.to_f64(t2)
     U.check(t2h, o.bn(t1h, inp.scale, inp.bias), wl.dtype, "bn pass")
     U.check(U.to_f64(y), o.silu(t2h), wl.dtype, "silu pass")
+
+
+def test_misaligned_pointers_fall_back(lib):
+    """A y that is element-aligned but not 16-byte aligned: AUTO still serves
+    the call (with a variant that needs no vector alignment) and the result is
+    right; forcing the vectorised pointwise variant is refused."""
+    import torch
+    wl = synth.Workload("misaligned", BF16, 2, 64, 8, 8, 48, 1, 1, 1, 0, "n01", 4242)
+    inp = synth.make_inputs(wl)
+    x, w, sc, bi = U.upload(inp)
+    n_out = wl.N * wl.C_out * wl.OH * wl.OW
+    buf = torch.empty(n_out + 8, dtype=torch.bfloat16, device="cuda")
+    y = buf[1:1 + n_out].view(wl.N, wl.C_out, wl.OH, wl.OW)
+    U.say("[misaligned] auto")
+    lib.conv_bn_silu(x, w, sc, bi, stride=1, pad=0, out=y)
+    torch.cuda.synchronize()
+    U.check(U.to_f64(y), U.oracle_full(inp), BF16, "misaligned auto")
+    with pytest.raises(lib.CbsError) as ei:
+        lib.conv_bn_silu(x, w, sc, bi, stride=1, pad=0, out=y, variant="pointwise")
+    assert ei.value.status == lib.ERR_UNSUPPORTED
