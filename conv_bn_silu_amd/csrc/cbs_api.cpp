@@ -101,6 +101,7 @@ bool variant_ok(int variant, const cbs::Shape &s, int dtype) {
         case CBS_VARIANT_GEMM_GATHER: return cbs::gemm_gather_supports(s, dtype);
         case CBS_VARIANT_GEMM_WINDOW: return cbs::window_supports(s, dtype);
         case CBS_VARIANT_POINTWISE: return cbs::pointwise_supports(s, dtype);
+        case CBS_VARIANT_SMALL_K: return cbs::stem_supports(s, dtype);
         case CBS_VARIANT_SCALAR: return cbs::scalar_supports(s, dtype);
         default: return false;
     }
@@ -110,6 +111,7 @@ bool variant_ok(int variant, const cbs::Shape &s, int dtype) {
 bool pointers_ok(int variant, const void *x, const void *w, const void *y) {
     switch (variant) {
         case CBS_VARIANT_POINTWISE: return cbs::pointwise_pointers_ok(x, w, y);
+        case CBS_VARIANT_SMALL_K: return cbs::stem_pointers_ok(x, w, y);
         default: return true;
     }
 }
@@ -123,6 +125,7 @@ int select(const cbs::Shape &s, int dtype, int num_cu) {
     const int64_t macs = (int64_t)s.M * s.C_out * s.K;
     if (macs <= (int64_t)1 << 21 && variant_ok(CBS_VARIANT_SCALAR, s, dtype)) return CBS_VARIANT_SCALAR;
     if (variant_ok(CBS_VARIANT_POINTWISE, s, dtype)) return CBS_VARIANT_POINTWISE;
+    if (variant_ok(CBS_VARIANT_SMALL_K, s, dtype)) return CBS_VARIANT_SMALL_K;
     if (variant_ok(CBS_VARIANT_GEMM_WINDOW, s, dtype)) return CBS_VARIANT_GEMM_WINDOW;
     return CBS_VARIANT_GEMM_GATHER;
 }
@@ -165,6 +168,7 @@ hipError_t launch(int variant, const cbs::Shape &s, int dtype, int epi, const vo
         case CBS_VARIANT_POINTWISE: return cbs::launch_pointwise(s, epi, x, w, scale, bias, y, st, num_cu);
         case CBS_VARIANT_GEMM_WINDOW:
             return cbs::launch_window(s, epi, x, w, scale, bias, y, workspace, st, num_cu);
+        case CBS_VARIANT_SMALL_K: return cbs::launch_stem(s, epi, x, w, scale, bias, y, st, num_cu);
         case CBS_VARIANT_SCALAR: return cbs::launch_scalar(s, dtype, epi, x, w, scale, bias, y, st);
         default: return hipErrorInvalidValue;
     }

@@ -32,6 +32,13 @@ size_t window_workspace_bytes(const Shape &s);
 hipError_t launch_window(const Shape &s, int epi, const void *x, const void *w, const float *scale,
                          const float *bias, void *y, void *workspace, hipStream_t st, int num_cu);
 
+// Small-K stem: 3x3, stride 2, pad 1, C_in <= 3, C_out <= 16 (bf16; W a
+// multiple of 32, OW <= 320); x and y 16-byte aligned.
+bool stem_supports(const Shape &s, int dtype);
+bool stem_pointers_ok(const void *x, const void *w, const void *y);
+hipError_t launch_stem(const Shape &s, int epi, const void *x, const void *w, const float *scale,
+                       const float *bias, void *y, hipStream_t st, int num_cu);
+
 // One output element per lane; any geometry, both dtypes.
 bool scalar_supports(const Shape &s, int dtype);
 hipError_t launch_scalar(const Shape &s, int dtype, int epi, const void *x, const void *w,

@@ -68,8 +68,9 @@ enum {
                                     channel block and reused by every kernel tap (bf16) */
     CBS_VARIANT_POINTWISE = 3,   /* 1x1, stride 1, pad 0: streams x once, all output
                                     channels per workgroup (bf16) */
-    CBS_VARIANT_SMALL_K = 4,     /* C_in*KH*KW <= 32 (e.g. an RGB stem): the whole
-                                    reduction in one MFMA step (bf16) */
+    CBS_VARIANT_SMALL_K = 4,     /* small reduction: the 3x3 stride-2 pad-1 RGB stem
+                                    (C_in <= 3, C_out <= 16, W a multiple of 32,
+                                    OW <= 320), K = 27 in one MFMA step (bf16) */
     CBS_VARIANT_SCALAR = 5,      /* one output element per lane, no tiling; small shapes */
     CBS_VARIANT_COUNT_ = 6
 };

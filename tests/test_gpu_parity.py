@@ -61,6 +61,13 @@ SWEEP = [
     (5, 256, 8, 8, 16, 1, 1, 1, 0),
     (1, 8, 1, 8, 1, 1, 1, 1, 0),
     (7, 128, 12, 12, 200, 1, 1, 1, 0),
+    # stems for the small-K variant: odd output-row counts, 1-3 channels,
+    # C_out below 16, each row width class, more images than compute units
+    (2, 3, 18, 64, 16, 3, 3, 2, 1),
+    (1, 1, 33, 96, 5, 3, 3, 2, 1),
+    (3, 2, 40, 640, 16, 3, 3, 2, 1),
+    (2, 3, 7, 160, 12, 3, 3, 2, 1),
+    (300, 3, 6, 32, 16, 3, 3, 2, 1),
 ]
 
 
@@ -87,7 +94,7 @@ def test_sweep(lib, case, dt, variant):
     U.check(U.to_f64(y), U.oracle_full(inp), dt, f"sweep{case}/{variant}")
 
 
-REDUCED = {"c1": {}, "c2": {"N": 1}, "c3": {"N": 1, "H": 96, "W": 80}, "c4": {"N": 1, "H": 130, "W": 98},
+REDUCED = {"c1": {}, "c2": {"N": 1}, "c3": {"N": 1, "H": 96, "W": 80}, "c4": {"N": 2, "H": 130},
            "c5": {"N": 3}}
 
 
