@@ -8,22 +8,31 @@
 // kernels for one operation": a GEMM tile would waste most of its columns on
 // so few output channels).
 //
-//  * One workgroup per compute unit owns a run of output rows of one image
-//    and walks it two output rows per step.
-//  * Input rows are kept in LDS as a ring of 16 row slots, each holding, per
-//    input channel, the row's "horizontal im2col": for tap column kw the
+//  * Workgroups of 4 waves, two per compute unit (their LDS fits twice), so
+//    one workgroup's loads and stores overlap the other's arithmetic.  Each
+//    computes one output row per step.  The G workgroups interleave over the
+//    N*OH output rows (workgroup j takes rows j, j+G, j+2G, ...), so at any
+//    time the whole chip reads and writes one contiguous window of x and y:
+//    DRAM pages stay open, which is worth about 10% of the bandwidth here
+//    over giving each workgroup its own run of rows.  The eight XCDs take
+//    contiguous slices of each window, so an input row shared by two
+//    neighbouring output rows is fetched into one L2.
+//  * The 3 input rows of a step are kept in LDS (3 sets of 3 row slots: the
+//    step being computed, the next being written, and the previous one that
+//    a slower wave may still read), each holding, per input channel, the
+//    row's "horizontal im2col": for tap column kw the
 //    array A_kw[ow] = x[ih][2*ow + kw - 1] (zero outside the row).  Built
 //    from 16-byte loads of 8 input columns, split into even and odd columns
-//    with byte permutes; the kw = 0 array, shifted by one column, comes from
-//    a second load 4 bytes earlier (or, at the row start, from the odd
-//    columns shifted in registers).
+//    with byte permutes; the kw = 0 array is the odd columns shifted by one,
+//    whose first element comes from the lane holding the previous 8 columns
+//    (a cross-lane permute; lane 0 fetches those 4 bytes itself).
 //  * The MFMA A fragment (16 pixels x 8 consecutive k per lane group) is two
 //    ds_read_b64_tr_b16 reads of four k-rows each: k = (ci, kh, kw) picks the
 //    array of input row 2*oh - 1 + kh, channel ci, tap kw; k >= 9*C_in reads
 //    a zero row.  The weights (B operand, 8 k values of one output channel
 //    per lane) stay in 4 VGPRs.
-//  * Two batches of 4 input rows are in flight in registers while a step
-//    computes; one barrier per step.
+//  * A step's input rows are loaded kStemPD steps ahead into registers; one
+//    barrier per step.
 //  * Epilogue (folded BN, SiLU, bf16) on the accumulators, staged per wave in
 //    LDS and stored as whole 16-byte pieces of output rows.
 #include <type_traits>
@@ -49,97 +58,122 @@ __device__ __forceinline__ void unroll(F &&f) {
     }
 }
 
-constexpr int kStemWaves = 8;
+constexpr int kStemWaves = 4;
 constexpr int kStemThreads = 64 * kStemWaves;
-constexpr int kRing = 16;  // input-row slots (a step reads 5 rows; 13 rows can be live)
+constexpr int kStemPD = 2;  // steps of input rows in flight in registers (>= 1)
+constexpr int kRing = 9;    // input-row slots: 3 steps x 3 rows (see the step loop)
 
 // Compile-time geometry for output rows of at most 64*NBW pixels (NBW:
-// 16-pixel blocks per wave per step of two rows).
+// 16-pixel blocks per wave per output row).
 template <int NBW>
 struct StemGeo {
-    static constexpr int OWMAX = 64 * NBW;
-    static constexpr int P = 2 * OWMAX + 32;       // bytes per im2col array (padding spreads banks)
-    static constexpr int SLOT = 9 * P + 64;        // bytes per input row: 3 channels x 3 taps
-    static constexpr int RINGB = kRing * SLOT;     // the zero row follows the ring
-    static constexpr int SP = 16 * NBW + 8;        // staging pitch (elements) per channel row
-    static constexpr int MAXT = (192 * NBW + kStemThreads - 1) / kStemThreads;  // loads per batch/thread
+    static constexpr int OWMAX = 16 * kStemWaves * NBW;
+    static constexpr int P = 2 * OWMAX + 32;   // bytes per im2col array (padding spreads banks)
+    static constexpr int SLOT = 9 * P + 64;    // bytes per input row: 3 channels x 3 taps
+    static constexpr int RINGB = kRing * SLOT; // the zero row follows the ring
+    static constexpr int SP = 16 * NBW + 8;    // staging pitch (elements) per channel row
+    // 16-byte copy tasks per thread per step: 3 rows x 3 channels x W/8.
+    static constexpr int MAXT = (3 * 3 * (2 * OWMAX / 8) + kStemThreads - 1) / kStemThreads;
 };
 
 template <int NBW, int EPI>
-__global__ __launch_bounds__(kStemThreads, 1) void stem_bf16(
+__global__ __launch_bounds__(kStemThreads, 2) void stem_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ scale,
-    const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int rows_per_wg, int wg_per_image) {
+    const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int wg_per_xcd) {
     using G = StemGeo<NBW>;
     __shared__ __attribute__((aligned(16))) char ring[G::RINGB + G::P];
     __shared__ __attribute__((aligned(16))) uint16_t stg[kStemWaves][16 * G::SP];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n = (int)blockIdx.x / wg_per_image;
-    const int r0 = ((int)blockIdx.x % wg_per_image) * rows_per_wg;
-    if (n >= s.N || r0 >= s.OH) return;  // uniform
-    const int r1 = min(r0 + rows_per_wg, s.OH);
-    const int steps = (r1 - r0 + 1) / 2;
+    // Block -> rank j among the G = 8*wg_per_xcd workgroups: XCD x (= block
+    // id mod 8) holds ranks x*wg_per_xcd .. +wg_per_xcd-1.  Step t computes
+    // global output row j + t*G (image n = row / OH, row oh = row mod OH).
+    const int gsz = 8 * wg_per_xcd;
+    const int j = ((int)blockIdx.x & 7) * wg_per_xcd + ((int)blockIdx.x >> 3);
+    const int rows_total = s.N * s.OH;
+    if (j >= rows_total) return;  // uniform
+    const int steps = (rows_total - j + gsz - 1) / gsz;
     const int bpr = s.OW / 16;      // 16-pixel blocks per output row
     const int segs = s.W / 8;       // 8-column input segments per row
-    const int tasks = 4 * s.C_in * segs;
+    const int tasks = 3 * s.C_in * segs;
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.C_in * s.H * s.W * 2u);
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)s.N * s.C_out * s.OHW * 2u);
 
-    // Input stream: row i of the stream is input row ih = 2*r0 - 1 + i.
-    // Batch b holds stream rows 4b-3 .. 4b; step t reads rows 4t .. 4t+4,
-    // i.e. batches t and t+1.  A row outside the image, or past the last one
-    // the workgroup reads, is not fetched (its loads return zeros).
-    u32x4 ra[2][G::MAXT], rs[2][G::MAXT];
-    auto load_batch = [&](int b, u32x4 (&a)[G::MAXT], u32x4 (&sh)[G::MAXT]) {
+    // Copy task q of this thread, task index tid + q*threads, is (input row
+    // kh of the step -- input row 2*oh - 1 + kh --, channel ci, 8-column
+    // segment seg).  Its place in x and in LDS is fixed but for the step.
+    // Consecutive lanes hold consecutive segments of one row unless seg == 0.
+    int tk_rr[G::MAXT], tk_lds[G::MAXT];
+    uint32_t tk_goff[G::MAXT];
+    bool tk_valid[G::MAXT], tk_first[G::MAXT];
+#pragma unroll
+    for (int q = 0; q < G::MAXT; ++q) {
+        const int t = tid + q * kStemThreads;
+        const int rr = t / (s.C_in * segs), rem = t - rr * (s.C_in * segs);
+        const int ci = rem / segs, seg = rem - ci * segs;
+        tk_valid[q] = t < tasks;
+        tk_first[q] = seg == 0;
+        tk_rr[q] = rr;
+        tk_goff[q] = (uint32_t)((ci * s.H + rr) * s.W + 8 * seg) * 2u;
+        tk_lds[q] = rr * G::SLOT + ci * 3 * G::P + 8 * seg;
+    }
+    const int prev_lane_addr = 4 * ((lane + 63) & 63);
+
+    // ra: x[8 seg .. 8 seg + 7]; rp: x[8 seg - 2 .. 8 seg - 1], fetched only
+    // by lane 0 (other lanes take it from their left neighbour).
+    u32x4 ra[kStemPD][G::MAXT];
+    uint32_t rp[kStemPD][G::MAXT];
+    auto load_step = [&](int t, u32x4 (&a)[G::MAXT], uint32_t (&pv)[G::MAXT]) {
+        const int row = j + t * gsz;  // uniform
+        const int nn = row / s.OH, oh = row - nn * s.OH;
+        const bool live = t < steps;
+        // First input row of the step, 2*oh - 1, relative to the image.
+        const int ih0 = 2 * oh - 1;
+        const uint32_t base = (uint32_t)((nn * s.C_in * s.H + ih0) * s.W) * 2u;
 #pragma unroll
         for (int q = 0; q < G::MAXT; ++q) {
-            const int t = tid + q * kStemThreads;
-            const int rr = t / (s.C_in * segs), rem = t - rr * (s.C_in * segs);
-            const int ci = rem / segs, seg = rem - ci * segs;
-            const int i = 4 * b - 3 + rr, ih = 2 * r0 - 1 + i;
-            const bool ok = t < tasks && i >= 0 && i <= 4 * steps && ih >= 0 && ih < s.H;
-            const uint32_t off = (uint32_t)(((n * s.C_in + ci) * s.H + ih) * s.W + 8 * seg) * 2u;
+            const int ih = ih0 + tk_rr[q];
+            const bool ok = live && tk_valid[q] && (uint32_t)ih < (uint32_t)s.H;
+            const uint32_t off = base + tk_goff[q];
             a[q] = buf_load16(xr, ok ? off : kOOB);
-            // x[8 seg - 2 .. 8 seg + 5]: its odd columns are the kw = 0 taps.
-            // Not needed at the row start (seg 0), where they come from `a`.
-            sh[q] = buf_load16(xr, ok && seg > 0 ? off - 4u : kOOB);
+            pv[q] = buf_load4(xr, ok && lane == 0 && !tk_first[q] ? off - 4u : kOOB);
         }
     };
-    // Scatter batch b into its ring slots: per (row, channel, segment) the
-    // even columns (kw = 1), odd columns (kw = 2) and the odd columns one to
-    // the left (kw = 0), 4 output pixels each.
-    auto write_batch = [&](int b, const u32x4 (&a)[G::MAXT], const u32x4 (&sh)[G::MAXT]) {
+    // Scatter step t's rows into its slot set: per (row, channel, segment)
+    // the even columns (kw = 1), odd columns (kw = 2) and the odd columns one
+    // to the left (kw = 0), 4 output pixels each.
+    auto write_step = [&](int t, const u32x4 (&a)[G::MAXT], const uint32_t (&pv)[G::MAXT]) {
+        char *const set = ring + (t % 3) * 3 * G::SLOT;
 #pragma unroll
         for (int q = 0; q < G::MAXT; ++q) {
-            const int t = tid + q * kStemThreads;
-            if (t >= tasks) continue;
-            const int rr = t / (s.C_in * segs), rem = t - rr * (s.C_in * segs);
-            const int ci = rem / segs, seg = rem - ci * segs;
-            const int i = 4 * b - 3 + rr;
-            char *dst = ring + (i & (kRing - 1)) * G::SLOT + ci * 3 * G::P + 8 * seg;
-            const u32x4 v = a[q], u = sh[q];
+            const u32x4 v = a[q];
             const uint32_t e0 = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);
             const uint32_t e1 = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
             const uint32_t o0 = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
             const uint32_t o1 = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
-            uint32_t l0 = __builtin_amdgcn_perm(u.y, u.x, 0x07060302u);
-            uint32_t l1 = __builtin_amdgcn_perm(u.w, u.z, 0x07060302u);
-            if (seg == 0) {  // left padding, then the odd columns shifted right by one
-                l0 = o0 << 16;
-                l1 = __builtin_amdgcn_alignbit(o1, o0, 16);
-            }
+            // Column 8 seg - 1 sits in the upper half of the left neighbour's
+            // o1 (or of lane 0's own fetch); zero at the row start.
+            uint32_t prev = (uint32_t)__builtin_amdgcn_ds_bpermute(prev_lane_addr, (int)o1);
+            prev = lane == 0 ? pv[q] : prev;
+            prev = tk_first[q] ? 0u : prev;
+            if (!tk_valid[q]) continue;
+            char *dst = set + tk_lds[q];
+            const uint32_t l0 = __builtin_amdgcn_perm(o0, prev, 0x05040302u);
+            const uint32_t l1 = __builtin_amdgcn_alignbit(o1, o0, 16);
             *(u32x2 *)(dst) = u32x2{l0, l1};
             *(u32x2 *)(dst + G::P) = u32x2{e0, e1};
             *(u32x2 *)(dst + 2 * G::P) = u32x2{o0, o1};
         }
     };
 
-    // Zero row (k >= 9*C_in and channels >= C_in read it).
+    // Zero row (k >= 9*C_in reads it).
     for (int i = tid; i < G::P / 16; i += kStemThreads) *(u32x4 *)(ring + G::RINGB + 16 * i) = u32x4{0, 0, 0, 0};
 
-    load_batch(0, ra[0], rs[0]);
-    load_batch(1, ra[1], rs[1]);
+    unroll<0, kStemPD>([&](auto bc) {
+        constexpr int b = decltype(bc)::value;
+        load_step(b, ra[b], rp[b]);
+    });
 
     // Transposed-read geometry of the 16x16x32 A operand: lane l holds pixel
     // l&15 of a block and k = 8*(l>>4) .. +7.  In read h (k = 8*(l>>4) + 4h
@@ -172,27 +206,48 @@ __global__ __launch_bounds__(kStemThreads, 1) void stem_bf16(
     const float sc = co < s.C_out ? scale[co] : 0.f, bi = co < s.C_out ? bias[co] : 0.f;
     const float sn = sc * -1.4426950408889634f, bn = bi * -1.4426950408889634f;
 
-    write_batch(0, ra[0], rs[0]);
-    load_batch(2, ra[0], rs[0]);
-    write_batch(1, ra[1], rs[1]);
-    load_batch(3, ra[1], rs[1]);
+    write_step(0, ra[0], rp[0]);
+    load_step(kStemPD, ra[0], rp[0]);
+
+    // This wave's blocks: block gb = wave*NBW + bb of a row starts at column
+    // 16*gb; blocks past bpr are idle (they read block 0, store nothing).
+    int blk_col[NBW];
+#pragma unroll
+    for (int bb = 0; bb < NBW; ++bb) {
+        const int gb = wave * NBW + bb;
+        blk_col[bb] = gb < bpr ? 32 * gb : 0;  // byte offset in an im2col array
+    }
+    // Store pieces (16 channel rows x 2*NBW pieces of 8 pixels per wave):
+    // LDS source and offset within the image's output (kOOB for an idle
+    // piece) are fixed; the image and row change per step.
+    constexpr int kStoreIt = (2 * 16 * NBW + 63) / 64;
+    uint32_t st_off[kStoreIt];
+    int st_lds[kStoreIt];
+#pragma unroll
+    for (int it = 0; it < kStoreIt; ++it) {
+        const int p = it * 64 + lane;
+        const int c = p / (2 * NBW), pc = p - c * (2 * NBW);
+        const int bb = pc >> 1, half = pc & 1;
+        const int gb = wave * NBW + bb;
+        const bool ok = p < 32 * NBW && gb < bpr && c < s.C_out;
+        st_lds[it] = (ok ? c : 0) * G::SP + 16 * bb + 8 * half;
+        st_off[it] = ok ? (uint32_t)(c * s.OHW + 16 * gb + 8 * half) * 2u : kOOB;
+    }
 
     uint16_t *const ow_ = stg[wave];
     auto compute = [&](int t) {
+        // Byte address of this lane's k-row for read h, before the block's
+        // column offset.
+        int base[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            base[h] = zero_of[h] ? G::RINGB + 8 * (jq & 3) : ((t % 3) * 3 + kh_of[h]) * G::SLOT + off_of[h];
         f32x4 acc[NBW];
 #pragma unroll
         for (int bb = 0; bb < NBW; ++bb) {
-            int gb = wave * NBW + bb;
-            if (gb >= 2 * bpr) gb = 0;  // idle block: read valid memory, store nothing
-            const int row = gb >= bpr ? 1 : 0, bx = gb - row * bpr;
-            u32x2 part[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int slot = (4 * t + 2 * row + kh_of[h]) & (kRing - 1);
-                const int a = zero_of[h] ? G::RINGB + 8 * (jq & 3) : slot * G::SLOT + off_of[h];
-                part[h] = lds_read_tr(ring + a + 32 * bx);
-            }
-            const bf16x8 af = __builtin_bit_cast(bf16x8, u32x4{part[0].x, part[0].y, part[1].x, part[1].y});
+            const u32x2 lo = lds_read_tr(ring + base[0] + blk_col[bb]);
+            const u32x2 hi = lds_read_tr(ring + base[1] + blk_col[bb]);
+            const bf16x8 af = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
             acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         }
         // Epilogue: lane holds channel co, pixels 4*grp .. +3 of each block.
@@ -214,35 +269,33 @@ __global__ __launch_bounds__(kStemThreads, 1) void stem_bf16(
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staging writes done
         __builtin_amdgcn_wave_barrier();
-        // Store: 16 channel rows x 2*NBW pieces of 8 pixels.
+        const int row = j + t * gsz;
+        const int nn = row / s.OH, oh = row - nn * s.OH;
+        const uint32_t obase = (uint32_t)((nn * s.C_out * s.OH + oh) * s.OW) * 2u;
 #pragma unroll
-        for (int it = 0; it < (2 * 16 * NBW + 63) / 64; ++it) {
-            const int p = it * 64 + lane;
-            const int c = p / (2 * NBW), pc = p - c * (2 * NBW);
-            const int bb = pc >> 1, half = pc & 1;
-            const int gb = wave * NBW + bb;
-            const int row = gb >= bpr ? 1 : 0, bx = gb - row * bpr;
-            const int oh = r0 + 2 * t + row;
-            const bool ok = p < 32 * NBW && gb < 2 * bpr && oh < r1 && c < s.C_out;
-            const u32x4 v = *(const u32x4 *)&ow_[(ok ? c : 0) * G::SP + 16 * bb + 8 * half];
-            const uint32_t off = (uint32_t)(((n * s.C_out + c) * s.OH + oh) * s.OW + 16 * bx + 8 * half) * 2u;
-            buf_store16(yr, ok ? off : kOOB, v);
+        for (int it = 0; it < kStoreIt; ++it) {
+            const u32x4 v = *(const u32x4 *)&ow_[st_lds[it]];
+            buf_store16(yr, st_off[it] == kOOB ? kOOB : obase + st_off[it], v);
         }
         __builtin_amdgcn_wave_barrier();
     };
 
-    // Step t: scatter batch t+2 (loaded two steps ago), request batch t+4,
-    // barrier (batch t+1 visible; slots of rows read two steps ago free),
-    // then compute output rows r0+2t, r0+2t+1.
-    for (int t = 0; t < steps; t += 2) {
-        unroll<0, 2>([&](auto dc) {
+    // Step t: scatter step t+1's rows (loaded kStemPD steps earlier) into
+    // slot set (t+1) mod 3, request step t+1+kStemPD's rows into the freed
+    // registers, barrier (step t's rows, written last step, become
+    // visible), then compute output row j + t*G.  The set written here was
+    // last read in step t-2, which every wave finished before the previous
+    // barrier.
+    for (int t0 = 0; t0 < steps; t0 += kStemPD) {
+        unroll<0, kStemPD>([&](auto dc) {
             constexpr int d = decltype(dc)::value;
-            const int tt = t + d;
-            if (tt >= steps) return;
-            write_batch(tt + 2, ra[d], rs[d]);
-            load_batch(tt + 4, ra[d], rs[d]);
+            constexpr int slot = (d + 1) % kStemPD;
+            const int t = t0 + d;
+            if (t >= steps) return;
+            write_step(t + 1, ra[slot], rp[slot]);
+            load_step(t + 1 + kStemPD, ra[slot], rp[slot]);
             __syncthreads();
-            compute(tt);
+            compute(t);
         });
     }
 }
@@ -250,17 +303,13 @@ __global__ __launch_bounds__(kStemThreads, 1) void stem_bf16(
 template <int NBW, int EPI>
 hipError_t launch_stem_t(const Shape &s, const void *x, const void *w, const float *scale, const float *bias,
                          void *y, hipStream_t st, int num_cu) {
-    // About one workgroup per compute unit: split each image's output rows
-    // into wg_per_image runs of an even number of rows.
-    int wg_per_image = num_cu / s.N;
-    if (wg_per_image < 1) wg_per_image = 1;
-    if (wg_per_image > (s.OH + 1) / 2) wg_per_image = (s.OH + 1) / 2;
-    int rows = (s.OH + wg_per_image - 1) / wg_per_image;
-    rows = (rows + 1) & ~1;
-    wg_per_image = (s.OH + rows - 1) / rows;
-    hipLaunchKernelGGL((stem_bf16<NBW, EPI>), dim3(s.N * wg_per_image), dim3(kStemThreads), 0, st,
-                       (const uint16_t *)x, (const uint16_t *)w, scale, bias, (uint16_t *)y, s, rows,
-                       wg_per_image);
+    // Two workgroups per compute unit (fewer if there are fewer rows).
+    const int rows_total = s.N * s.OH;
+    int wgs = 2 * num_cu;
+    if (wgs > rows_total) wgs = rows_total;
+    const int wg_per_xcd = (wgs + 7) / 8;
+    hipLaunchKernelGGL((stem_bf16<NBW, EPI>), dim3(8 * wg_per_xcd), dim3(kStemThreads), 0, st,
+                       (const uint16_t *)x, (const uint16_t *)w, scale, bias, (uint16_t *)y, s, wg_per_xcd);
     return hipGetLastError();
 }
 
