@@ -100,6 +100,7 @@ bool variant_ok(int variant, const cbs::Shape &s, int dtype) {
     switch (variant) {
         case CBS_VARIANT_GEMM_GATHER: return cbs::gemm_gather_supports(s, dtype);
         case CBS_VARIANT_GEMM_WINDOW: return cbs::window_supports(s, dtype);
+        case CBS_VARIANT_GEMM_WINDOW32: return cbs::window32_supports(s, dtype);
         case CBS_VARIANT_POINTWISE: return cbs::pointwise_supports(s, dtype);
         case CBS_VARIANT_SMALL_K: return cbs::stem_supports(s, dtype);
         case CBS_VARIANT_SCALAR: return cbs::scalar_supports(s, dtype);
@@ -126,6 +127,9 @@ int select(const cbs::Shape &s, int dtype, int num_cu) {
     if (macs <= (int64_t)1 << 21 && variant_ok(CBS_VARIANT_SCALAR, s, dtype)) return CBS_VARIANT_SCALAR;
     if (variant_ok(CBS_VARIANT_POINTWISE, s, dtype)) return CBS_VARIANT_POINTWISE;
     if (variant_ok(CBS_VARIANT_SMALL_K, s, dtype)) return CBS_VARIANT_SMALL_K;
+    // Channel-heavy layers whose tiles fill the 32x32 blocks well.
+    if (s.C_in >= 128 && variant_ok(CBS_VARIANT_GEMM_WINDOW32, s, dtype) && cbs::window32_efficiency(s) >= 800)
+        return CBS_VARIANT_GEMM_WINDOW32;
     if (variant_ok(CBS_VARIANT_GEMM_WINDOW, s, dtype)) return CBS_VARIANT_GEMM_WINDOW;
     return CBS_VARIANT_GEMM_GATHER;
 }
@@ -168,6 +172,8 @@ hipError_t launch(int variant, const cbs::Shape &s, int dtype, int epi, const vo
         case CBS_VARIANT_POINTWISE: return cbs::launch_pointwise(s, epi, x, w, scale, bias, y, st, num_cu);
         case CBS_VARIANT_GEMM_WINDOW:
             return cbs::launch_window(s, epi, x, w, scale, bias, y, workspace, st, num_cu);
+        case CBS_VARIANT_GEMM_WINDOW32:
+            return cbs::launch_window32(s, epi, x, w, scale, bias, y, workspace, st, num_cu);
         case CBS_VARIANT_SMALL_K: return cbs::launch_stem(s, epi, x, w, scale, bias, y, st, num_cu);
         case CBS_VARIANT_SCALAR: return cbs::launch_scalar(s, dtype, epi, x, w, scale, bias, y, st);
         default: return hipErrorInvalidValue;
@@ -244,7 +250,7 @@ int conv_bn_silu_run_variant(conv_bn_silu_t h, int variant, const void *x, const
     if (variant == CBS_VARIANT_AUTO) variant = select_for_call(s, dtype, h->num_cu, x, w, y);
     else if (!variant_ok(variant, s, dtype) || !pointers_ok(variant, x, w, y)) return CBS_ERR_UNSUPPORTED;
     void *ws = nullptr;
-    if (variant == CBS_VARIANT_GEMM_WINDOW) {
+    if (variant == CBS_VARIANT_GEMM_WINDOW || variant == CBS_VARIANT_GEMM_WINDOW32) {
         rc = record_hip(h, ensure_workspace(h, cbs::window_workspace_bytes(s), &ws));
         if (rc != CBS_OK) return rc;
     }
@@ -281,7 +287,7 @@ int conv_bn_silu_run_unfused(conv_bn_silu_t h, const void *x, const void *w, con
     const hipStream_t st = (hipStream_t)stream;
     const int variant = select_for_call(s, dtype, h->num_cu, x, w, t1);
     void *ws = nullptr;
-    if (variant == CBS_VARIANT_GEMM_WINDOW) {
+    if (variant == CBS_VARIANT_GEMM_WINDOW || variant == CBS_VARIANT_GEMM_WINDOW32) {
         rc = record_hip(h, ensure_workspace(h, cbs::window_workspace_bytes(s), &ws));
         if (rc != CBS_OK) return rc;
     }
@@ -346,6 +352,7 @@ const char *conv_bn_silu_variant_name(int variant) {
         case CBS_VARIANT_POINTWISE: return "pointwise";
         case CBS_VARIANT_SMALL_K: return "small_k";
         case CBS_VARIANT_SCALAR: return "scalar";
+        case CBS_VARIANT_GEMM_WINDOW32: return "gemm_window32";
         default: return "unknown";
     }
 }

@@ -39,6 +39,19 @@ bool stem_pointers_ok(const void *x, const void *w, const void *y);
 hipError_t launch_stem(const Shape &s, int epi, const void *x, const void *w, const float *scale,
                        const float *bias, void *y, hipStream_t st, int num_cu);
 
+// Packs OIHW weights for the window kernels: wp[co][block][tap][32
+// channels] (zero past C_in), window_workspace_bytes() long.
+hipError_t launch_pack_weights(const Shape &s, const void *w, void *workspace, hipStream_t st);
+
+// Window-staged implicit GEMM on 32x32x16 MFMA with 7 x 2 accumulator tiles
+// per wave (bf16; W, OW multiples of 4); same workspace as the window kernel.
+// window32_efficiency: share (per mille) of a tile's matrix work that lands
+// on real output pixels.
+bool window32_supports(const Shape &s, int dtype);
+int window32_efficiency(const Shape &s);
+hipError_t launch_window32(const Shape &s, int epi, const void *x, const void *w, const float *scale,
+                           const float *bias, void *y, void *workspace, hipStream_t st, int num_cu);
+
 // One output element per lane; any geometry, both dtypes.
 bool scalar_supports(const Shape &s, int dtype);
 hipError_t launch_scalar(const Shape &s, int dtype, int epi, const void *x, const void *w,

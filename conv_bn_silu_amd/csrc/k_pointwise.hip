@@ -5,25 +5,31 @@
 // (page "Fusing an Epilogue", section "The problem") means streaming x and y
 // through the chip exactly once.  This kernel is built for that:
 //
-//  * Persistent, statically balanced workgroups, one per compute unit, of 8
-//    waves (two per SIMD).  Each owns a pixel range of P pixels (P a multiple
-//    of 8, about M / #ranges) and a tile of 256 output channels, so every
-//    compute unit moves the same number of bytes and there is no tail of
-//    half-empty tile waves.  It walks its range in chunks of CP pixels.
-//  * XCD-aware placement: each XCD runs a contiguous run of pixel ranges (and
-//    every channel tile of them), so cache lines shared by neighbouring
-//    ranges, and x re-read by several channel tiles, meet in one L2.
-//  * The weights of each wave's 32 channels stay in VGPRs for the whole
-//    kernel (they are the B operand of every MFMA, 16 bytes per lane each).
+//  * Persistent workgroups, one per compute unit, of 8 waves (two per SIMD),
+//    each with a tile of 256 output channels.  The pixels are cut into
+//    chunks of CP and dealt round-robin: workgroup rank j computes chunks
+//    j, j + G, j + 2G, ... (G ranks), so the whole chip streams through x
+//    and y as one contiguous front (see the kernel for why that matters).
+//  * XCD-aware placement: consecutive ranks run on one XCD, so chunks that
+//    share cache lines, and x re-read by several channel tiles, meet in one
+//    L2.
+//  * The weight tile (256 channels x C_in) is fetched once per workgroup with
+//    LDS DMA in coalesced pieces, then each wave keeps its 32 channels in
+//    VGPRs for the whole kernel (the B operand of every MFMA, 16 bytes per
+//    lane each).
 //  * The products run on v_mfma_f32_32x32x16_bf16 (32 pixels x 32 channels x
 //    16 k per instruction), the shape that sustains the matrix-core rate with
 //    one wave per SIMD.
-//  * x chunks are copied into LDS in their NCHW order ([channel][pixel], 16
-//    bytes per lane), and the MFMA A fragments -- eight consecutive channels
-//    of one pixel per lane -- are produced by ds_read_b64_tr_b16, which
-//    transposes 4x16 blocks of 16-bit values across each 16-lane group.  Rows
-//    are padded so that the four rows a group reads fall in distinct banks.
-//  * Three chunks of x are in flight in registers while one is computed.
+//  * x chunks are stored in LDS as channel records: per 32-channel block,
+//    one 64-byte record per pixel, its four 16-byte octets XOR-swizzled with
+//    bits 1..2 of the pixel index.  An MFMA A fragment -- eight consecutive
+//    channels of one pixel per lane -- is then one ds_read_b128, and the 32
+//    pixels x 2 octets that a wave reads at once hit distinct banks.  (On
+//    gfx950 a transposed ds_read_b64_tr_b16 moves about a quarter of the
+//    bytes per cycle of a plain 16-byte read, so the transposition is done
+//    in registers while staging instead: a task loads 8 channels x 8 pixels,
+//    16 bytes per channel, and writes 8 records' octets.)
+//  * Two chunks of x are in flight in registers while one is computed.
 //  * The epilogue (folded BN, SiLU, bf16 rounding) runs on the accumulators;
 //    each wave stages its 32-channel output tile in LDS and writes y in whole
 //    128-byte rows, 16 bytes per lane.
@@ -34,14 +40,6 @@
 
 namespace cbs {
 namespace {
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ u32x2 ds_read_tr(const uint16_t *lds_elem) {
-    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4 *)(lds_elem));
-    return __builtin_bit_cast(u32x2, v);
-}
 
 // Calls f(integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, typename F>
@@ -65,13 +63,13 @@ __device__ __forceinline__ PixPos advance(PixPos a, int d, int hw) {
     }
     return r;
 }
-__device__ __forceinline__ PixPos chunk_start(PixPos start0, int offset, int hw) {
-    PixPos c = start0;
-    while (offset >= hw) {  // uniform; only for images smaller than a chunk
-        offset -= hw;
-        ++c.n;
-    }
-    return advance(c, offset, hw);
+
+// Byte offset of octet `octet` (0..3) of the 64-byte record of pixel `px`
+// within a record block: the octets are XOR-swizzled with bits 1..2 of the
+// pixel so that 8 consecutive lanes reading one octet of 8 consecutive
+// pixels, and the staging writes, spread over the banks.
+__device__ __forceinline__ uint32_t rec_off(int px, int octet) {
+    return (uint32_t)px * 64u + (((uint32_t)octet ^ ((uint32_t)px >> 1)) & 3u) * 16u;
 }
 
 constexpr int kWaves = 8;               // wave w owns output channels [32w, 32w+32) of the tile
@@ -83,90 +81,101 @@ constexpr int kTileCo = 32 * kWaves;    // output channels per workgroup
 template <int KS, int CP, int PD, int EPI>
 __global__ __launch_bounds__(kThreadsPw, 1) void pointwise_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ scale,
-    const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int px_per_wg, int co_tiles,
-    int n_ranges, int ranges_per_xcd) {
-    constexpr int ROW = CP + 16;                       // x chunk: LDS elements per channel row
+    const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int co_tiles, int ranks_per_xcd,
+    int n_ranks) {
     constexpr int KP = KS * 16;                        // channels held in LDS (zero beyond C_in)
-    constexpr int TASKS = (KP * (CP / 8) + kThreadsPw - 1) / kThreadsPw;  // 16-byte copies per thread
+    constexpr int NKB = (KP + 31) / 32;                // 32-channel record blocks
+    constexpr int KBB = CP * 64;                       // bytes per record block of a chunk
+    constexpr int NTASK = (KP / 8) * (CP / 8);         // staging tasks: 8 channels x 8 pixels
+    static_assert(NTASK <= kThreadsPw, "one staging task per thread at most");
     constexpr int MB = CP / 32;                        // 32-pixel blocks per chunk
     constexpr int OROW = CP + 8;                       // output staging: elements per channel row
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][KP * ROW];
-    __shared__ __attribute__((aligned(16))) uint16_t os[kWaves][32 * OROW];
+    // One LDS area, used first for the workgroup's weight tile (kTileCo
+    // channels x KP, loaded with LDS DMA) and then for the x chunks and the
+    // output staging.
+    constexpr int OCT = KP / 8;                        // 16-byte octets per weight row
+    constexpr int W_BYTES = kTileCo * KP * 2;
+    constexpr int XS_BYTES = 2 * NKB * KBB;
+    constexpr int OS_BYTES = kWaves * 32 * OROW * 2;
+    constexpr int LDS_BYTES = W_BYTES > XS_BYTES + OS_BYTES ? W_BYTES : XS_BYTES + OS_BYTES;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+    unsigned char(*const xs)[NKB * KBB] = (unsigned char(*)[NKB * KBB])lds;
+    uint16_t(*const os)[32 * OROW] = (uint16_t(*)[32 * OROW])(lds + XS_BYTES);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // Block id -> (pixel range, channel tile), XCD-aware.  The XCDs take
-    // workgroups round-robin (XCD = id % 8), so XCD x gets a contiguous run
-    // of ranges_per_xcd pixel ranges and all channel tiles of each: ranges
-    // that share cache lines at their ends, and the tiles that read the same
-    // x, meet in one L2.
-    int wg, ct;
+    // Work: the M pixels in chunks of CP, chunk c = j + t*n_ranks going to
+    // rank j (its t-th chunk) of channel tile ct.  At any time the ranks
+    // together read one contiguous stretch of every channel plane of x (and
+    // write one of y), which keeps DRAM pages open; giving each workgroup a
+    // run of its own spreads the accesses over every plane instead and
+    // costs several microseconds of first-access latency.  XCD-aware: the
+    // XCDs take blocks round-robin (XCD = block id % 8), and XCD x holds
+    // ranks x*ranks_per_xcd .. +ranks_per_xcd-1 of every channel tile, so
+    // neighbouring chunks (which share cache lines) meet in one L2.
+    int j, ct;
     {
         const int b = (int)blockIdx.x;
         const int xcd = b & 7, slot = b >> 3;
         ct = slot % co_tiles;
-        const int idx = slot / co_tiles;
-        if (idx >= ranges_per_xcd) return;  // uniform
-        wg = xcd * ranges_per_xcd + idx;
-        if (wg >= n_ranges) return;  // uniform
+        j = xcd * ranks_per_xcd + slot / co_tiles;
+        if (slot / co_tiles >= ranks_per_xcd || j >= n_ranks) return;  // uniform
     }
     const int co_lane = ct * kTileCo + wave * 32 + (lane & 31);  // this lane's output channel
-    const int m_begin = wg * px_per_wg;
-    const int m_end = min(m_begin + px_per_wg, s.M);
-    if (m_begin >= m_end) return;  // uniform across the workgroup
+    const int n_total = (s.M + CP - 1) / CP;
+    if (j >= n_total) return;  // uniform
+    const int n_chunks = (n_total - j + n_ranks - 1) / n_ranks;  // chunks of this rank
     const int hw = s.HW;
+    auto chunk_pos = [&](int c) {  // first pixel of this rank's chunk c (uniform)
+        const int m = (j + c * n_ranks) * CP;
+        const int n = m / hw;
+        return PixPos{n, m - n * hw};
+    };
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.C_in * hw * 2u);
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)s.N * s.C_out * hw * 2u);
 
-    u32x4 wf[KS];  // weights, filled after the first x requests
+    u32x4 wf[KS];  // weights (B fragments), from the LDS weight tile
     float sc, bi, sn, bn;
 
-    const PixPos start0{m_begin / hw, m_begin - (m_begin / hw) * hw};
-    const int n_chunks = (m_end - m_begin + CP - 1) / CP;
 
-    // Copy task t: channel ci = t / (CP/8), 8-pixel piece t % (CP/8).  A piece
-    // outside the workgroup's range, a channel past C_in, or a chunk past the
-    // last, gets an out-of-range offset: the load returns zeros and costs no
-    // memory traffic.
-    auto load_chunk = [&](int c, u32x4 (&r)[TASKS]) {
-        const PixPos c0 = chunk_start(start0, c * CP, hw);
-        const int mc = m_begin + c * CP;
+    // Staging task t < NTASK: channel octet o = t / (CP/8) (channels 8o ..
+    // 8o+7), 8-pixel piece t % (CP/8).  A piece outside the workgroup's
+    // range, a channel past C_in, or a chunk past the last, gets an
+    // out-of-range offset: the load returns zeros and costs no memory
+    // traffic.
+    const bool stager = tid < NTASK;
+    const int st_o = tid / (CP / 8), st_piece = tid % (CP / 8);
+    auto load_chunk = [&](int c, u32x4 (&r)[8]) {
+        const PixPos c0 = chunk_pos(c);
+        const int mc = (j + c * n_ranks) * CP;
+        const PixPos pp = advance(c0, 8 * st_piece, hw);
+        const bool ok = stager && c < n_chunks && mc + 8 * st_piece < s.M;
+        const uint32_t off0 = (uint32_t)((pp.n * s.C_in + 8 * st_o) * hw + pp.p) * 2u;
 #pragma unroll
-        for (int q = 0; q < TASKS; ++q) {
-            const int t = tid + q * kThreadsPw;
-            const int ci = t / (CP / 8), piece = t % (CP / 8);
-            const PixPos pp = advance(c0, 8 * piece, hw);
-            const bool ok = ci < s.C_in && mc + 8 * piece < m_end;
-            r[q] = buf_load16(xr, ok ? (uint32_t)((pp.n * s.C_in + ci) * hw + pp.p) * 2u : kOOB);
+        for (int c8 = 0; c8 < 8; ++c8)
+            r[c8] = buf_load16(xr, ok && 8 * st_o + c8 < s.C_in ? off0 + (uint32_t)(c8 * hw) * 2u : kOOB);
+    };
+    // Transpose a task's 8 channels x 8 pixels and write the pixels' octets.
+    auto store_chunk = [&](int buf, const u32x4 (&r)[8]) {
+        if (!stager) return;
+        unsigned char *blk = &xs[buf][(st_o >> 2) * KBB];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            u32x4 v;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t lo = r[2 * d][p >> 1], hi = r[2 * d + 1][p >> 1];
+                v[d] = (p & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u) : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            }
+            *(u32x4 *)(blk + rec_off(8 * st_piece + p, st_o & 3)) = v;
         }
     };
-    auto store_chunk = [&](int buf, const u32x4 (&r)[TASKS]) {
-#pragma unroll
-        for (int q = 0; q < TASKS; ++q) {
-            const int t = tid + q * kThreadsPw;
-            const int ci = t / (CP / 8), piece = t % (CP / 8);
-            if (TASKS * kThreadsPw == KP * (CP / 8) || ci < KP)
-                *(u32x4 *)&xs[buf][ci * ROW + 8 * piece] = r[q];
-        }
-    };
 
-    // Transposed-read geometry for the 32x32x16 A operand (lane l: pixel
-    // l&31, channels 8*(l>>5) .. +7 of the slice): 16-lane group G = l>>4
-    // covers pixels 16*(G&1) .. +15 and channel half G>>1; lane j = l&15 of
-    // the group reads channel row 8*(G>>1) + (j>>2) (+4 for the upper four)
-    // at pixel column 16*(G&1) + 4*(j&3).
-    const int grp = lane >> 4, jl = lane & 15;
-    const int tr_row = 8 * (grp >> 1) + (jl >> 2);
-    const int tr_col = 16 * (grp & 1) + 4 * (jl & 3);
+    // A fragment of 16-channel slice ks for 32-pixel block i (32x32x16: lane
+    // l holds pixel l&31, channels 16*ks + 8*(l>>5) .. +7).
     uint16_t *const ow = os[wave];
-
-    // MFMAs of one chunk into `acc` (MB 32-pixel blocks).  The A fragments
-    // of slice ks+PFD are read while the MFMAs of slice ks run.
     auto read_a = [&](int buf, int ks, int i) {
-        const uint16_t *base = &xs[buf][(16 * ks + tr_row) * ROW + 32 * i + tr_col];
-        const u32x2 lo = ds_read_tr(base);
-        const u32x2 hi = ds_read_tr(base + 4 * ROW);
-        return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        return *(const bf16x8 *)(&xs[buf][(ks >> 1) * KBB + rec_off(32 * i + (lane & 31), 2 * (ks & 1) + (lane >> 5))]);
     };
     auto mfma_chunk = [&](int buf, f32x16 (&acc)[MB]) {
         constexpr int PFD = 2;
@@ -223,8 +232,8 @@ __global__ __launch_bounds__(kThreadsPw, 1) void pointwise_bf16(
     auto epi_store = [&](int c, bool live) {
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's staging writes are done
         __builtin_amdgcn_wave_barrier();
-        const PixPos c0 = chunk_start(start0, (live ? c : 0) * CP, hw);
-        const int mc = m_begin + c * CP;
+        const PixPos c0 = chunk_pos(live ? c : 0);
+        const int mc = (j + (live ? c : 0) * n_ranks) * CP;
         constexpr int PIECES = CP / 8;          // 16-byte pieces per channel row
         constexpr int ROWS_PER = 64 / PIECES;   // rows covered by one wave-wide pass
 #pragma unroll
@@ -233,7 +242,7 @@ __global__ __launch_bounds__(kThreadsPw, 1) void pointwise_bf16(
             const u32x4 v = *(const u32x4 *)&ow[r * OROW + 8 * piece];
             const PixPos pp = advance(c0, 8 * piece, hw);
             const int co = ct * kTileCo + wave * 32 + r;
-            const bool ok = live && mc + 8 * piece < m_end && co < s.C_out;
+            const bool ok = live && mc + 8 * piece < s.M && co < s.C_out;
             buf_store16(yr, ok ? (uint32_t)((pp.n * s.C_out + co) * hw + pp.p) * 2u : kOOB, v);
         }
         __builtin_amdgcn_wave_barrier();  // staging reads done before the tile is rewritten
@@ -246,24 +255,50 @@ __global__ __launch_bounds__(kThreadsPw, 1) void pointwise_bf16(
     // n_chunks no current one (its MFMAs run on zeros and are discarded):
     // keeping both halves unconditional keeps them in one basic block, so
     // the scheduler can interleave MFMAs with the epilogue's VALU work.
-    u32x4 r[PD][TASKS];
+    // Weight tile first, with LDS DMA: rows co0 .. co0+255 of w, KP channels
+    // each (zeros past C_out or C_in), 16-byte octet o of row r stored in
+    // slot r*OCT + (o ^ (r & SW)): 16 lanes reading one octet of 16
+    // consecutive rows hit 16 distinct bank groups, and each DMA instruction
+    // still fetches contiguous pieces of a few rows.  Lane i of a DMA
+    // instruction writes slot base + i, so the slot decides what it fetches.
+    constexpr int SW = (OCT < 16 ? OCT : 16) - 1;
+    {
+        const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)s.C_out * s.C_in * 2u);
+        const int co0 = ct * kTileCo;
+#pragma unroll
+        for (int j = 0; j < kTileCo * OCT / kThreadsPw; ++j) {
+            const int slot = j * kThreadsPw + tid;
+            const int r = slot / OCT, o = (slot % OCT) ^ (r & SW);
+            const int co = co0 + r, k = 8 * o;
+            const uint32_t off = (co < s.C_out && k < s.C_in) ? (uint32_t)(co * s.C_in + k) * 2u : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wr, (__attribute__((address_space(3))) void *)(lds + (j * kThreadsPw + wave * 64) * 16), 16, off, 0, 0,
+                0);
+        }
+    }
+    u32x4 r[PD][8];
 #pragma unroll
     for (int d = 0; d < PD; ++d) load_chunk(d, r[d]);
 
-    // Weights (B operand of the 32x32x16 MFMA): lane holds channel co_lane
-    // and k = 16*ks + 8*(lane>>5) .. +7; fetched after the first chunks of x
-    // have been requested so that their latency overlaps the x stream.  The
-    // epilogue constants are folded: v = acc*sc + bi, -v*log2(e) = acc*sn + bn.
+    // The epilogue constants are folded: v = acc*sc + bi, -v*log2(e) =
+    // acc*sn + bn.
     sc = co_lane < s.C_out ? scale[co_lane] : 0.f;
     bi = co_lane < s.C_out ? bias[co_lane] : 0.f;
     sn = sc * -1.4426950408889634f;
     bn = bi * -1.4426950408889634f;
+
+    // Weights into registers (B operand of the 32x32x16 MFMA): lane holds
+    // channel co_lane and k = 16*ks + 8*(lane>>5) .. +7.  Octets past C_in
+    // are forced to zero whatever the LDS holds.
+    __builtin_amdgcn_s_waitcnt(0);  // the DMA above (and the first x chunks) have landed
+    __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        const int k = 16 * ks + 8 * (lane >> 5);
-        wf[ks] = (co_lane < s.C_out && k < s.C_in) ? *(const u32x4 *)(w + co_lane * s.C_in + k)
-                                                   : u32x4{0u, 0u, 0u, 0u};
+        const int rrow = wave * 32 + (lane & 31), o = 2 * ks + (lane >> 5);
+        const u32x4 v = *(const u32x4 *)(lds + (rrow * OCT + (o ^ (rrow & SW))) * 16);
+        wf[ks] = 8 * o < s.C_in ? v : u32x4{0u, 0u, 0u, 0u};
     }
+    __syncthreads();  // the weight tile's LDS is reused for x from here on
 
     f32x16 acc0[MB], acc1[MB];
 #pragma unroll
@@ -307,17 +342,15 @@ template <int KS, int CP, int PD, int EPI>
 hipError_t launch_pw(const Shape &s, const void *x, const void *w, const float *scale, const float *bias,
                      void *y, hipStream_t st, int num_cu) {
     const int co_tiles = (s.C_out + kTileCo - 1) / kTileCo;
-    // One workgroup per compute unit in total, split over the channel
-    // tiles; each owns a balanced run of pixels (a multiple of 8).
-    int n_ranges = (num_cu + co_tiles - 1) / co_tiles;
-    int px_per_wg = (s.M + n_ranges - 1) / n_ranges;
-    px_per_wg = (px_per_wg + 7) / 8 * 8;
-    n_ranges = (s.M + px_per_wg - 1) / px_per_wg;
-    const int ranges_per_xcd = (n_ranges + 7) / 8;
-    const int blocks = ranges_per_xcd * 8 * co_tiles;
+    // One workgroup per compute unit in total, split over the channel tiles.
+    const int n_total = (s.M + CP - 1) / CP;
+    int n_ranks = (num_cu + co_tiles - 1) / co_tiles;
+    if (n_ranks > n_total) n_ranks = n_total;
+    const int ranks_per_xcd = (n_ranks + 7) / 8;
+    const int blocks = ranks_per_xcd * 8 * co_tiles;
     hipLaunchKernelGGL((pointwise_bf16<KS, CP, PD, EPI>), dim3(blocks), dim3(kThreadsPw), 0, st,
-                       (const uint16_t *)x, (const uint16_t *)w, scale, bias, (uint16_t *)y, s, px_per_wg,
-                       co_tiles, n_ranges, ranges_per_xcd);
+                       (const uint16_t *)x, (const uint16_t *)w, scale, bias, (uint16_t *)y, s, co_tiles,
+                       ranks_per_xcd, n_ranks);
     return hipGetLastError();
 }
 
@@ -339,8 +372,8 @@ hipError_t launch_pointwise(const Shape &s, int epi, const void *x, const void *
     const int ks = (s.C_in + 15) / 16;
 #define CBS_PW(KS_)                                                                              \
     if (ks <= KS_)                                                                               \
-        return epi == kFused ? launch_pw<KS_, 32, 4, kFused>(s, x, w, scale, bias, y, st, num_cu) \
-                             : launch_pw<KS_, 32, 4, kConvOnly>(s, x, w, scale, bias, y, st, num_cu);
+        return epi == kFused ? launch_pw<KS_, 32, 2, kFused>(s, x, w, scale, bias, y, st, num_cu) \
+                             : launch_pw<KS_, 32, 2, kConvOnly>(s, x, w, scale, bias, y, st, num_cu);
     CBS_PW(4) CBS_PW(8) CBS_PW(16)
 #undef CBS_PW
     return hipErrorInvalidValue;

@@ -380,18 +380,22 @@ size_t window_workspace_bytes(const Shape &s) {
     return (size_t)s.C_out * ((s.C_in + kCK - 1) / kCK) * s.T * 64;
 }
 
+hipError_t launch_pack_weights(const Shape &s, const void *w, void *workspace, hipStream_t st) {
+    const int n_chunks = (s.C_in + kCK - 1) / kCK;
+    const int pack_total = s.C_out * n_chunks * s.T * 4;
+    const int pack_blocks = (pack_total + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(pack_weights_bf16, dim3(pack_blocks < 4096 ? pack_blocks : 4096), dim3(kThreads), 0, st,
+                       (const uint16_t *)w, (uint16_t *)workspace, s, n_chunks);
+    return hipGetLastError();
+}
+
 hipError_t launch_window(const Shape &s, int epi, const void *x, const void *w, const float *scale,
                          const float *bias, void *y, void *workspace, hipStream_t st, int num_cu) {
     const Config &cfg = pick_config(s);
     const int wgs_per_cu = cfg.mbw == 5 ? 2 : 1;
     WinGeo g;
     if (!plan(s, cfg, num_cu, wgs_per_cu, &g)) return hipErrorInvalidValue;
-    const int n_chunks = g.n_chunks;
-    const int pack_total = s.C_out * n_chunks * s.T * 4;
-    const int pack_blocks = (pack_total + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(pack_weights_bf16, dim3(pack_blocks < 4096 ? pack_blocks : 4096), dim3(kThreads), 0, st,
-                       (const uint16_t *)w, (uint16_t *)workspace, s, n_chunks);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_pack_weights(s, w, workspace, st);
     if (e != hipSuccess) return e;
     const dim3 grid(g.n_wg), block(kThreads);
     auto xx = (const uint16_t *)x;

@@ -72,7 +72,9 @@ enum {
                                     (C_in <= 3, C_out <= 16, W a multiple of 32,
                                     OW <= 320), K = 27 in one MFMA step (bf16) */
     CBS_VARIANT_SCALAR = 5,      /* one output element per lane, no tiling; small shapes */
-    CBS_VARIANT_COUNT_ = 6
+    CBS_VARIANT_GEMM_WINDOW32 = 6, /* as GEMM_WINDOW on 32x32x16 MFMA with larger tiles
+                                      per wave: channel-heavy layers (bf16) */
+    CBS_VARIANT_COUNT_ = 7
 };
 
 typedef struct conv_bn_silu_handle *conv_bn_silu_t;

@@ -68,6 +68,15 @@ SWEEP = [
     (3, 2, 40, 640, 16, 3, 3, 2, 1),
     (2, 3, 7, 160, 12, 3, 3, 2, 1),
     (300, 3, 6, 32, 16, 3, 3, 2, 1),
+    # channel-heavy 3x3 layers for the 32x32 window variant: whole-image
+    # tiles, several tiles per image with ragged edges, partial channel
+    # blocks, two output-channel tiles, stride 2, a 5x5 filter
+    (2, 64, 20, 20, 128, 3, 3, 1, 1),
+    (1, 96, 12, 16, 200, 3, 3, 1, 1),
+    (2, 40, 16, 12, 64, 3, 3, 1, 1),
+    (1, 128, 24, 24, 64, 3, 3, 2, 1),
+    (3, 64, 36, 8, 48, 5, 5, 1, 2),
+    (2, 32, 30, 28, 96, 3, 3, 1, 1),
 ]
 
 
