@@ -124,7 +124,7 @@ bool pointers_ok(int variant, const void *x, const void *w, const void *y) {
 int select(const cbs::Shape &s, int dtype, int num_cu) {
     (void)num_cu;
     const int64_t macs = (int64_t)s.M * s.C_out * s.K;
-    if (macs <= (int64_t)1 << 21 && variant_ok(CBS_VARIANT_SCALAR, s, dtype)) return CBS_VARIANT_SCALAR;
+    if (macs <= (int64_t)1 << 23 && variant_ok(CBS_VARIANT_SCALAR, s, dtype)) return CBS_VARIANT_SCALAR;
     if (variant_ok(CBS_VARIANT_POINTWISE, s, dtype)) return CBS_VARIANT_POINTWISE;
     if (variant_ok(CBS_VARIANT_SMALL_K, s, dtype)) return CBS_VARIANT_SMALL_K;
     // Channel-heavy layers whose tiles fill the 32x32 blocks well.

@@ -12,22 +12,25 @@
 // owns pixel blocks wm*MB .. wm*MB+MB-1 (32 pixels each, pixel p of the tile
 // = row p / TW, column p mod TW) and output channels 64*wn .. +63.
 //
-// Reduction order: channel block (32 channels), then tap groups of TG taps,
-// then the tap, then two 16-channel halves.  LDS holds two window buffers
-// (this channel block and the next) and two weight buffers (this tap group
-// and the next); one barrier per tap group.  Window records and the weight
-// tile use the same 64-byte, XOR-swizzled record layout as the 16x16 window
-// kernel (one record = 32 channels of one input position or one output
-// channel), so a fragment -- 8 consecutive channels of one pixel or one
-// output channel per lane -- is one 16-byte LDS read.
+// Reduction order: channel block (32 channels), then the tap (a "unit"),
+// then two 16-channel halves.  LDS holds two window buffers (this channel
+// block and the next) and two weight buffers (this tap and the next); one
+// barrier per unit.  A record holds 32 channels of one input position
+// (window) or one output channel (weights) in 64 bytes, padded to 80: with 5
+// 16-byte slots per record, 16 lanes reading one slot of 16 consecutive
+// records hit 16 distinct bank groups of gfx950's 64-bank LDS, and a
+// fragment -- 8 consecutive channels of one pixel or one output channel per
+// lane -- is one ds_read_b128 whose per-tap part of the address is a
+// uniform offset.
 //
-// Fragment layouts (32x32x16): A lane l: pixel l&31 of the block, channels
-// 8*(l>>5) .. +7 of the half; B lane l: output channel l&31, same channels;
-// D lane l: output channel l&31, pixels 8*(i>>2) + 4*(l>>5) + (i&3) for
-// accumulator element i.
-//
-// Epilogue: folded BN + SiLU on the accumulators, bf16 rounding, 8-byte
-// stores of 4 consecutive pixels of one channel (TW is a multiple of 4).
+// Staging is through registers and runs well ahead of use, so that the
+// load latency hides behind the matrix work of one workgroup per CU: a
+// tap's weights (128 channels x 64 bytes, 2 x 16 bytes per thread) are
+// requested three units ahead (a ring of three register sets; the unit loop
+// is unrolled by three), and the next channel block's whole window (up to 3
+// parts of 256 tasks, each task 8 channels x VEC columns, transposed with
+// byte permutes) is requested at the start of a block and written at its
+// end.
 #include <type_traits>
 
 #include "cbs_device.h"
@@ -40,8 +43,10 @@ namespace {
 constexpr int kThreads32 = 256;
 constexpr int kBN32 = 128;            // output channels per tile
 constexpr int kCK32 = 32;             // input channels per block
-constexpr int kFpBytes32 = 33 * 1024; // one window buffer
-constexpr int kTG = 3;                // taps per weight group
+constexpr int kRec = 80;              // bytes per record (64 data + 16 padding)
+constexpr int kFpBytes32 = 41 * 1024; // one window buffer
+constexpr int kWTB = kBN32 * kRec;    // one weight buffer: one tap x 128 records
+constexpr int kParts = 3;             // window parts (256 tasks each) at most
 
 // Calls f(integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, typename F>
@@ -50,10 +55,6 @@ __device__ __forceinline__ void static_for(F &&f) {
         f(std::integral_constant<int, B>{});
         static_for<B + 1, E>(f);
     }
-}
-
-__device__ __forceinline__ uint32_t rec_addr32(uint32_t rec, uint32_t octet) {
-    return rec * 64u + ((octet ^ (rec >> 1)) & 3u) * 16u;
 }
 
 __device__ __forceinline__ uint32_t pair16(uint32_t lo_word, uint32_t hi_word, int h) {
@@ -75,10 +76,8 @@ template <int MB, int VEC, int EPI>
 __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wp, const float *__restrict__ scale,
     const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, WinGeo g) {
-    constexpr int WTB = kTG * kBN32 * 64;  // weight buffer: TG taps x 128 channels x 64 bytes
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kFpBytes32 + 2 * WTB];
-    unsigned char *const fpb = lds;
-    unsigned char *const wbb = lds + 2 * kFpBytes32;
+    __shared__ __attribute__((aligned(16))) unsigned char fps[2][kFpBytes32];
+    __shared__ __attribute__((aligned(16))) unsigned char wbs[2][kWTB];
     typedef typename XV32<VEC>::T XT;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -89,8 +88,9 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     const int t_end = min(t_begin + g.tiles_per_wg, g.n_tiles);
     if (t_begin >= t_end) return;  // uniform
     const int steps = (t_end - t_begin) * g.n_chunks;  // (tile, channel block) pairs
-    const int ngroups = (s.T + kTG - 1) / kTG;
-    const int units = steps * ngroups;                 // (tile, channel block, tap group)
+    const int upt = g.n_chunks * s.T;                  // units (channel block, tap) per tile
+    const int upt3 = (upt + 2) / 3 * 3;                // padded to a multiple of 3 (tail units idle)
+    const int units = (t_end - t_begin) * upt3;
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.C_in * s.HW * 2u);
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)s.C_out * g.n_chunks * s.T * 64u);
@@ -111,41 +111,55 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         r.co0 = ct * kBN32;
         return r;
     };
+    // Unit u -> (step, tap); a tile's padding units have none.
+    struct Unit {
+        int step, tap;
+        bool real;
+    };
+    auto unit_of = [&](int u) {
+        const int tl = u / upt3, k = u - tl * upt3;
+        Unit r;
+        r.real = u < units && k < upt;
+        const int kk = k < upt ? k : upt - 1;
+        r.step = tl * g.n_chunks + kk / s.T;
+        r.tap = kk % s.T;
+        return r;
+    };
 
     // ---- window staging ----------------------------------------------------
-    // Task t: octet t&3, row parity (t>>2)&1, column group (t>>3) % ncg, row
-    // pair (t>>3) / ncg.  Part f of a window is tasks f*256 + tid; the parts
-    // of the next block's window are staged one per tap group.
+    // Task t (part f = t / 256): octet o = t&3, row parity (t>>2)&1, column
+    // group (t>>3) % ncg, row pair (t>>3) / ncg.
+    const int nparts = (((g.FR + 1) / 2) * g.ncg * 8 + kThreads32 - 1) / kThreads32;  // <= kParts
     auto fp_load = [&](int step, int f, XT (&reg)[8]) {
         const int tile = t_begin + step / g.n_chunks;
         const int ck = step % g.n_chunks;
-        const bool live = step < steps;
+        const bool live = step < steps && f < nparts;
         const Tile tl = tile_of(live ? tile : t_begin);
         const int iw_lo = tl.ow0 * s.stride - s.pad;
         const int g0 = (iw_lo >= 0 ? iw_lo / VEC : -((-iw_lo + VEC - 1) / VEC)) * VEC;
         const int t = tid + f * kThreads32;
-        const int o = t & 3, rr = (t >> 2) & 1, rest = t >> 3;
-        const int cg = rest % g.ncg, r = 2 * (rest / g.ncg) + rr;
+        const int rest = t >> 3, o = t & 3;
+        const int cg = rest % g.ncg, r = 2 * (rest / g.ncg) + ((t >> 2) & 1);
         const int ih = tl.oh0 * s.stride - s.pad + r;
         const int iw0 = g0 + cg * VEC;
         const bool ok = live && r < g.FR && (unsigned)ih < (unsigned)s.H && iw0 >= 0 && iw0 < s.W &&
                         iw0 + VEC - 1 >= iw_lo && iw0 <= iw_lo + g.FC - 1;
+        const uint32_t off0 = (uint32_t)(((tl.n * s.C_in + ck * kCK32 + 8 * o) * s.H + ih) * s.W + iw0) * 2u;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const int ci = ck * kCK32 + 8 * o + c;
-            const uint32_t off =
-                (ok && ci < s.C_in) ? (uint32_t)(((tl.n * s.C_in + ci) * s.H + ih) * s.W + iw0) * 2u : kOOB;
-            reg[c] = XV32<VEC>::load(xr, off);
+            reg[c] = XV32<VEC>::load(xr, (ok && ci < s.C_in) ? off0 + (uint32_t)(c * s.HW) * 2u : kOOB);
         }
     };
     auto fp_store = [&](int step, int f, unsigned char *fp, const XT (&reg)[8]) {
+        if (f >= nparts) return;  // uniform
         const int tile = t_begin + step / g.n_chunks;
         const Tile tl = tile_of(step < steps ? tile : t_begin);
         const int iw_lo = tl.ow0 * s.stride - s.pad;
         const int g0 = (iw_lo >= 0 ? iw_lo / VEC : -((-iw_lo + VEC - 1) / VEC)) * VEC;
         const int t = tid + f * kThreads32;
-        const int o = t & 3, rr = (t >> 2) & 1, rest = t >> 3;
-        const int cg = rest % g.ncg, r = 2 * (rest / g.ncg) + rr;
+        const int rest = t >> 3, o = t & 3;
+        const int cg = rest % g.ncg, r = 2 * (rest / g.ncg) + ((t >> 2) & 1);
         if (r >= g.FR) return;
         const int c0 = g0 + cg * VEC - iw_lo;  // window column of the group's first element (> -VEC)
         const int c0p = c0 + VEC * s.stride;
@@ -162,51 +176,46 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
             u32x4 v;
 #pragma unroll
             for (int d = 0; d < 4; ++d) v[d] = pair16(reg[2 * d][j >> 1], reg[2 * d + 1][j >> 1], j & 1);
-            *(u32x4 *)(fp + rec_addr32((uint32_t)pos, (uint32_t)o)) = v;
+            *(u32x4 *)(fp + pos * kRec + o * 16) = v;
         }
     };
-    const int nparts = (((g.FR + 1) / 2) * g.ncg * 8 + kThreads32 - 1) / kThreads32;  // <= ngroups
 
-    // ---- weight staging: unit u = (step, tap group); TG taps x 128 channels
-    // x 4 octets; thread piece q: tap q>>1 of the group, channel ((q&1)*256 +
-    // tid) >> 2, octet tid & 3 -------------------------------------------------
-    auto w_load = [&](int u, u32x4 (&reg)[2 * kTG]) {
-        const int step = u / ngroups, grp = u - step * ngroups;
-        const int tile = t_begin + step / g.n_chunks;
-        const int ck = step % g.n_chunks;
+    // ---- weight staging: one tap x 128 channels x 4 octets; thread piece q
+    // (0, 1): channel (q*256 + tid) >> 2, octet tid & 3 ----------------------
+    auto w_load = [&](int u, u32x4 (&reg)[2]) {
+        const Unit un = unit_of(u);
+        const int tile = t_begin + un.step / g.n_chunks;
+        const int ck = un.step % g.n_chunks;
         const int co0 = (tile % g.co_tiles) * kBN32;
 #pragma unroll
-        for (int q = 0; q < 2 * kTG; ++q) {
-            const int tap = grp * kTG + (q >> 1);
-            const int p = (q & 1) * kThreads32 + tid;
+        for (int q = 0; q < 2; ++q) {
+            const int p = q * kThreads32 + tid;
             const int co = co0 + (p >> 2);
-            const bool ok = u < units && tap < s.T && co < s.C_out;
-            reg[q] = buf_load16(wr, ok ? (uint32_t)(((co * g.n_chunks + ck) * s.T + tap) * 64 + (p & 3) * 16)
+            const bool ok = un.real && co < s.C_out;
+            reg[q] = buf_load16(wr, ok ? (uint32_t)(((co * g.n_chunks + ck) * s.T + un.tap) * 64 + (p & 3) * 16)
                                        : kOOB);
         }
     };
-    auto w_store = [&](unsigned char *wb, const u32x4 (&reg)[2 * kTG]) {
+    auto w_store = [&](unsigned char *wb, const u32x4 (&reg)[2]) {
 #pragma unroll
-        for (int q = 0; q < 2 * kTG; ++q) {
-            const int p = (q & 1) * kThreads32 + tid;
-            *(u32x4 *)(wb + rec_addr32((uint32_t)((q >> 1) * kBN32 + (p >> 2)), (uint32_t)(p & 3))) = reg[q];
+        for (int q = 0; q < 2; ++q) {
+            const int p = q * kThreads32 + tid;
+            *(u32x4 *)(wb + (p >> 2) * kRec + (p & 3) * 16) = reg[q];
         }
     };
 
     // ---- per-lane fragment geometry ----------------------------------------
     const int tile_px = g.TH * g.TW;
-    int base[MB];
+    uint32_t abase[MB];  // byte address of this lane's pixel record (tap (0,0)), octet hi
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
         const int px = (wm * MB + b) * 32 + l32;
         const int i = px / g.TW, j = px - (px / g.TW) * g.TW;
-        base[b] = px < tile_px ? i * s.stride * g.FCP + j : 0;
+        abase[b] = (uint32_t)((px < tile_px ? i * s.stride * g.FCP + j : 0) * kRec + hi * 16);
     }
-    uint32_t baddr[2][2];  // [channel block][half]: weight record of this lane, before the tap
+    uint32_t bbase[2];  // weight record of this lane, octet hi
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) baddr[cb][h] = rec_addr32((uint32_t)(wn * 64 + 32 * cb + l32), (uint32_t)(2 * h + hi));
+    for (int cb = 0; cb < 2; ++cb) bbase[cb] = (uint32_t)((wn * 64 + 32 * cb + l32) * kRec + hi * 16);
 
     f32x16 acc[MB][2];
 #pragma unroll
@@ -216,79 +225,80 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[b][cb][e] = 0.f;
 
-    // Prologue: window of step 0 and weights of unit 0 into LDS buffers 0;
-    // part 0 of step 1's window and unit 1's weights in flight.
-    XT fpr[8];
-    u32x4 wreg[2 * kTG];
-    w_load(0, wreg);
-    for (int f = 0; f < nparts; ++f) {
-        fp_load(0, f, fpr);
-        fp_store(0, f, fpb, fpr);
-    }
-    w_store(wbb, wreg);
-    fp_load(1, 0, fpr);
-    w_load(1, wreg);
+    // Prologue: window of step 0 and weights of unit 0 into buffers 0;
+    // weights of units 1 and 2 in flight in ring slots 1 and 2.
+    XT fpr[kParts][8];
+    u32x4 wreg[3][2];
+    w_load(0, wreg[0]);
+    static_for<0, kParts>([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        fp_load(0, f, fpr[f]);
+    });
+    w_load(1, wreg[1]);
+    w_load(2, wreg[2]);
+    static_for<0, kParts>([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        fp_store(0, f, fps[0], fpr[f]);
+    });
+    w_store(wbs[0], wreg[0]);
     __syncthreads();
 
-    // The unit's taps run as 2*TG half-steps (tap, 16-channel half); the
-    // fragments of half-step i+1 are read from LDS while the 2*MB matrix
-    // instructions of half-step i run (two fragment sets, A0/B0 and A1/B1).
+    // Unit u (ring slot u mod 3): request unit u+3's weights; at a block's
+    // first tap request the next block's window; the two half-steps (the
+    // second's fragments read while the first's 2*MB matrix instructions
+    // run); write unit u+1's weights, and after a block's last tap the next
+    // window; barrier.
     bf16x8 fa[2][MB], fb[2][2];
-    int u = 0;
-    for (int step = 0; step < steps; ++step) {
-        const unsigned char *fp = fpb + (step & 1) * kFpBytes32;
-        int kh = 0, kw = 0;  // first tap of the current group
-        for (int grp = 0; grp < ngroups; ++grp, ++u) {
-            const unsigned char *wb = wbb + (u & 1) * WTB;
-            // Window offsets of the group's taps (taps past T are skipped).
-            int toff[kTG];
-            bool tval[kTG];
+    auto run_unit = [&](int u, auto slot_c) {
+        constexpr int sl = decltype(slot_c)::value;
+        const Unit un = unit_of(u);
+        w_load(u + 3, wreg[sl]);
+        const bool first = un.real && un.tap == 0;
+        const bool last = un.real && un.tap == s.T - 1;
+        if (first) {
+            static_for<0, kParts>([&](auto fc) {
+                constexpr int f = decltype(fc)::value;
+                fp_load(un.step + 1, f, fpr[f]);
+            });
+        }
+        if (un.real) {
+            const unsigned char *fp = fps[un.step & 1];
+            const unsigned char *wb = wbs[u & 1];
+            const int kh = un.tap / s.KW, kw = un.tap - kh * s.KW;
+            const int toff = (kh * g.FCP + (kw % s.stride) * g.CS + kw / s.stride) * kRec;
+            static_for<0, 2>([&](auto hc) {
+                constexpr int h = decltype(hc)::value;
 #pragma unroll
-            for (int tt = 0; tt < kTG; ++tt) {
-                tval[tt] = grp * kTG + tt < s.T;
-                toff[tt] = kh * g.FCP + (kw % s.stride) * g.CS + kw / s.stride;
-                if (++kw == s.KW) {
-                    kw = 0;
-                    ++kh;
-                }
-            }
-            auto load_half = [&](int tt, int h, bf16x8 (&A)[MB], bf16x8 (&Bf)[2]) {
+                for (int cb = 0; cb < 2; ++cb) fb[h][cb] = *(const bf16x8 *)(wb + bbase[cb] + 32 * h);
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb) Bf[cb] = *(const bf16x8 *)(wb + tt * (kBN32 * 64) + baddr[cb][h]);
+                for (int b = 0; b < MB; ++b) fa[h][b] = *(const bf16x8 *)(fp + abase[b] + toff + 32 * h);
+            });
+            static_for<0, 2>([&](auto hc) {
+                constexpr int h = decltype(hc)::value;
 #pragma unroll
                 for (int b = 0; b < MB; ++b)
-                    A[b] = *(const bf16x8 *)(fp + rec_addr32((uint32_t)(base[b] + toff[tt]), (uint32_t)(2 * h + hi)));
-            };
-            load_half(0, 0, fa[0], fb[0]);
-            static_for<0, 2 * kTG>([&](auto ic) {
-                constexpr int i = decltype(ic)::value;
-                constexpr int cur = i & 1, nxt = cur ^ 1;
-                if constexpr (i + 1 < 2 * kTG) {
-                    if (tval[(i + 1) >> 1]) load_half((i + 1) >> 1, (i + 1) & 1, fa[nxt], fb[nxt]);
-                }
-                if (tval[i >> 1]) {
 #pragma unroll
-                    for (int b = 0; b < MB; ++b)
-#pragma unroll
-                        for (int cb = 0; cb < 2; ++cb)
-                            acc[b][cb] =
-                                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][b], fb[cur][cb], acc[b][cb], 0, 0, 0);
-                }
+                    for (int cb = 0; cb < 2; ++cb)
+                        acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[h][b], fb[h][cb], acc[b][cb], 0, 0, 0);
             });
-            // Stage the next unit's weights and one part of the next block's
-            // window into buffers nobody reads now, then request the next.
-            w_store(wbb + ((u + 1) & 1) * WTB, wreg);
-            w_load(u + 2, wreg);
-            if (grp < nparts) {
-                fp_store(step + 1, grp, fpb + ((step + 1) & 1) * kFpBytes32, fpr);
-                if (grp + 1 < nparts)
-                    fp_load(step + 1, grp + 1, fpr);
-                else
-                    fp_load(step + 2, 0, fpr);
-            }
-            __syncthreads();
         }
-        if ((step + 1) % g.n_chunks != 0) continue;
+        w_store(wbs[(u + 1) & 1], wreg[(sl + 1) % 3]);
+        if (last) {
+            static_for<0, kParts>([&](auto fc) {
+                constexpr int f = decltype(fc)::value;
+                fp_store(un.step + 1, f, fps[(un.step + 1) & 1], fpr[f]);
+            });
+        }
+        __syncthreads();
+    };
+
+    for (int tile = t_begin; tile < t_end; ++tile) {
+        const int u0 = (tile - t_begin) * upt3;
+        for (int k = 0; k < upt3; k += 3) {
+            run_unit(u0 + k, std::integral_constant<int, 0>{});
+            run_unit(u0 + k + 1, std::integral_constant<int, 1>{});
+            run_unit(u0 + k + 2, std::integral_constant<int, 2>{});
+        }
 
         // ---- epilogue for the finished tile --------------------------------
         // (The tile width is passed through an empty asm so that the pixel
@@ -296,7 +306,7 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         // into registers the reduction needs.)
         int tw_e = g.TW;
         asm volatile("" : "+s"(tw_e));
-        const Tile tl = tile_of(t_begin + step / g.n_chunks);
+        const Tile tl = tile_of(tile);
         float sc[2], bi[2];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
@@ -351,11 +361,11 @@ bool make_geo32(const Shape &s, int TH, int TW, const Config32 &cfg, int num_cu,
     g->CS = (g->FC + s.stride - 1) / s.stride;
     g->FCP = s.stride * g->CS;
     if (g->FCP % 2 == 0) g->FCP += 1;
-    if ((int64_t)g->FR * g->FCP * 64 > kFpBytes32) return false;
+    if ((int64_t)g->FR * g->FCP * kRec > kFpBytes32) return false;
     g->ncg = (g->FC - 1 + cfg.vec - 1) / cfg.vec + 1;
     const int tasks = ((g->FR + 1) / 2) * g->ncg * 8;
-    // the next block's window is staged one part (256 tasks) per tap group
-    if (tasks > kThreads32 * ((s.T + kTG - 1) / kTG)) return false;
+    // the next block's window is staged in at most kParts parts of 256 tasks
+    if (tasks > kParts * kThreads32) return false;
     g->tiles_h = (s.OH + TH - 1) / TH;
     g->tiles_w = (s.OW + TW - 1) / TW;
     g->co_tiles = (s.C_out + kBN32 - 1) / kBN32;
