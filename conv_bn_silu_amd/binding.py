@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libconv_bn_silu.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_HIP, ERR_BAD_HANDLE = range(6)
 DTYPE_F32, DTYPE_BF16 = 0, 1
 VARIANTS = {"auto": 0, "gemm_gather": 1, "gemm_window": 2, "pointwise": 3, "small_k": 4, "scalar": 5,
-            "gemm_window32": 6}
+            "gemm_window32": 6, "strided_rows": 7}
 
 # Every symbol the header declares; the CPU tests check the library exports each.
 EXPORTS = [

@@ -103,6 +103,7 @@ bool variant_ok(int variant, const cbs::Shape &s, int dtype) {
         case CBS_VARIANT_GEMM_WINDOW32: return cbs::window32_supports(s, dtype);
         case CBS_VARIANT_POINTWISE: return cbs::pointwise_supports(s, dtype);
         case CBS_VARIANT_SMALL_K: return cbs::stem_supports(s, dtype);
+        case CBS_VARIANT_ROWS: return cbs::rows_supports(s, dtype);
         case CBS_VARIANT_SCALAR: return cbs::scalar_supports(s, dtype);
         default: return false;
     }
@@ -113,6 +114,7 @@ bool pointers_ok(int variant, const void *x, const void *w, const void *y) {
     switch (variant) {
         case CBS_VARIANT_POINTWISE: return cbs::pointwise_pointers_ok(x, w, y);
         case CBS_VARIANT_SMALL_K: return cbs::stem_pointers_ok(x, w, y);
+        case CBS_VARIANT_ROWS: return cbs::rows_pointers_ok(x, w, y);
         default: return true;
     }
 }
@@ -127,6 +129,7 @@ int select(const cbs::Shape &s, int dtype, int num_cu) {
     if (macs <= (int64_t)1 << 23 && variant_ok(CBS_VARIANT_SCALAR, s, dtype)) return CBS_VARIANT_SCALAR;
     if (variant_ok(CBS_VARIANT_POINTWISE, s, dtype)) return CBS_VARIANT_POINTWISE;
     if (variant_ok(CBS_VARIANT_SMALL_K, s, dtype)) return CBS_VARIANT_SMALL_K;
+    if (variant_ok(CBS_VARIANT_ROWS, s, dtype)) return CBS_VARIANT_ROWS;
     // Channel-heavy layers whose tiles fill the 32x32 blocks well.
     if (s.C_in >= 128 && variant_ok(CBS_VARIANT_GEMM_WINDOW32, s, dtype) && cbs::window32_efficiency(s) >= 800)
         return CBS_VARIANT_GEMM_WINDOW32;
@@ -175,6 +178,7 @@ hipError_t launch(int variant, const cbs::Shape &s, int dtype, int epi, const vo
         case CBS_VARIANT_GEMM_WINDOW32:
             return cbs::launch_window32(s, epi, x, w, scale, bias, y, workspace, st, num_cu);
         case CBS_VARIANT_SMALL_K: return cbs::launch_stem(s, epi, x, w, scale, bias, y, st, num_cu);
+        case CBS_VARIANT_ROWS: return cbs::launch_rows(s, epi, x, w, scale, bias, y, st, num_cu);
         case CBS_VARIANT_SCALAR: return cbs::launch_scalar(s, dtype, epi, x, w, scale, bias, y, st);
         default: return hipErrorInvalidValue;
     }
@@ -353,6 +357,7 @@ const char *conv_bn_silu_variant_name(int variant) {
         case CBS_VARIANT_SMALL_K: return "small_k";
         case CBS_VARIANT_SCALAR: return "scalar";
         case CBS_VARIANT_GEMM_WINDOW32: return "gemm_window32";
+        case CBS_VARIANT_ROWS: return "strided_rows";
         default: return "unknown";
     }
 }

@@ -39,6 +39,14 @@ bool stem_pointers_ok(const void *x, const void *w, const void *y);
 hipError_t launch_stem(const Shape &s, int epi, const void *x, const void *w, const float *scale,
                        const float *bias, void *y, hipStream_t st, int num_cu);
 
+// 3x3 stride-2 pad-1 layers with C_in a multiple of 16 up to 64 (bf16; W a
+// multiple of 8, OW a multiple of 4 and at most 160); x, w, y 16-byte
+// aligned.
+bool rows_supports(const Shape &s, int dtype);
+bool rows_pointers_ok(const void *x, const void *w, const void *y);
+hipError_t launch_rows(const Shape &s, int epi, const void *x, const void *w, const float *scale, const float *bias,
+                       void *y, hipStream_t st, int num_cu);
+
 // Packs OIHW weights for the window kernels: wp[co][block][tap][32
 // channels] (zero past C_in), window_workspace_bytes() long.
 hipError_t launch_pack_weights(const Shape &s, const void *w, void *workspace, hipStream_t st);

@@ -1,0 +1,313 @@
+// k_rows.hip -- 3x3, stride-2, padding-1 layers with a moderate channel
+// count (C_in a multiple of 16, up to 64): the downsampling convolutions of
+// a detector backbone.  Bound by streaming x in and y out.
+//
+// The GEMM view is the one of "Fusing an Epilogue" (section "Three kernels
+// for one operation"), with the reduction k = (ci, kh, kw) in the OIHW order
+// of w.  The A operand comes from LDS by transposed reads
+// (ds_read_b64_tr_b16), which need the four pixels a lane loads to be
+// adjacent and 8-byte aligned in LDS; with stride 2 the pixels of one tap
+// are every other input column, so each input row is stored as three
+// "horizontal im2col" arrays, one per tap column:
+//     A_kw[ow] = x[ih][2*ow + kw - 1]   (zero outside the row),
+// i.e. the odd columns shifted by one (kw = 0), the even columns (kw = 1)
+// and the odd columns (kw = 2).  Array (ci, kh, kw) is row k of a
+// [k][pixel] matrix, so a 16-k step of the MFMA reads 16 consecutive rows.
+//
+//  * Workgroups of 4 waves, one per CU; wave w owns output channels
+//    32w .. 32w+31 of the workgroup's 128-channel tile and all OW pixels of
+//    the output row being computed (NB blocks of 32, v_mfma_f32_32x32x16_bf16).
+//  * The G workgroups of a channel tile interleave over the N*OH output rows
+//    (rank j takes rows j, j+G, ...): at any time the chip streams one
+//    contiguous window of x and y, which keeps DRAM pages open.
+//  * A unit is (output row, 16-channel chunk): its 48 input row segments
+//    are loaded two units ahead into registers (16-byte loads of 8 columns,
+//    split into even and odd columns with byte permutes; the shifted odd
+//    array takes its first element from the left neighbour lane), written
+//    to one of three LDS sets one unit ahead, and read by the unit after a
+//    barrier.
+//  * The unit's weights (32 channels x 144 k per wave, 9 fragments of 16
+//    bytes per lane) are loaded one unit ahead into registers.
+//  * Row pitch in LDS: 2*OW bytes, an odd multiple of 64 for OW = 32*NB
+//    with NB odd (and padded to one otherwise), so the four rows a 16-lane
+//    group reads fall in distinct quarters of the 64 banks.
+//  * Epilogue after a row's last chunk: folded BN + SiLU, bf16, 8-byte
+//    stores of 4 consecutive pixels of one channel.
+#include <type_traits>
+
+#include "cbs_device.h"
+#include "cbs_launch.h"
+
+namespace cbs {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 rows_tr(const unsigned char *p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void rows_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        rows_for<B + 1, E>(f);
+    }
+}
+
+constexpr int kRowsWaves = 4;
+constexpr int kRowsThreads = 64 * kRowsWaves;
+constexpr int kRowsTile = 32 * kRowsWaves;  // output channels per workgroup
+constexpr int kChunk = 16;                  // input channels per unit
+constexpr int kKRows = kChunk * 9;          // k rows per unit (144 = 9 MFMA steps of 16)
+constexpr int kRowsPD = 2;                  // units of input in flight in registers
+constexpr int kSets = 3;                    // LDS sets of k rows
+
+template <int NB>
+struct RowsGeo {
+    static constexpr int OWMAX = 32 * NB;
+    static constexpr int P = (NB % 2 == 1) ? 2 * OWMAX : 2 * OWMAX + 64;  // row pitch, odd multiple of 64
+    static constexpr int SET = kKRows * P;                                // bytes per set
+    // 16-byte tasks per unit: 3 input rows x 16 channels x (2*OWMAX)/8 segments
+    static constexpr int TASKS = 3 * kChunk * (2 * OWMAX / 8);
+    static constexpr int MAXT = (TASKS + kRowsThreads - 1) / kRowsThreads;
+};
+
+template <int NB, int EPI>
+__global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ scale,
+    const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int co_tiles, int ranks_per_xcd,
+    int n_ranks) {
+    using G = RowsGeo<NB>;
+    __shared__ __attribute__((aligned(16))) unsigned char sets[kSets * G::SET];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int j, ct;
+    {
+        const int b = (int)blockIdx.x;
+        const int xcd = b & 7, slot = b >> 3;
+        ct = slot % co_tiles;
+        j = xcd * ranks_per_xcd + slot / co_tiles;
+        if (slot / co_tiles >= ranks_per_xcd || j >= n_ranks) return;  // uniform
+    }
+    const int rows_total = s.N * s.OH;
+    if (j >= rows_total) return;  // uniform
+    const int steps = (rows_total - j + n_ranks - 1) / n_ranks;  // output rows of this rank
+    const int nchunks = s.C_in / kChunk;
+    const int units = steps * nchunks;
+    const int segs = s.W / 8;
+    const int tasks = 3 * kChunk * segs;
+
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.C_in * s.H * s.W * 2u);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)s.C_out * s.K * 2u);
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)s.N * s.C_out * s.OHW * 2u);
+
+    // Copy task q of this thread (index tid + q*threads): input row kh of the
+    // unit, channel ci of the chunk, 8-column segment seg.  Consecutive lanes
+    // hold consecutive segments of one row unless seg == 0.
+    int tk_kh[G::MAXT], tk_lds[G::MAXT];
+    uint32_t tk_goff[G::MAXT];
+    bool tk_valid[G::MAXT], tk_first[G::MAXT];
+#pragma unroll
+    for (int q = 0; q < G::MAXT; ++q) {
+        const int t = tid + q * kRowsThreads;
+        const int kh = t / (kChunk * segs), rem = t - kh * (kChunk * segs);
+        const int ci = rem / segs, seg = rem - ci * segs;
+        tk_valid[q] = t < tasks;
+        tk_first[q] = seg == 0;
+        tk_kh[q] = kh;
+        tk_goff[q] = (uint32_t)((ci * s.H + kh) * s.W + 8 * seg) * 2u;
+        tk_lds[q] = (ci * 9 + kh * 3) * G::P + 8 * seg;
+    }
+    const int prev_lane_addr = 4 * ((lane + 63) & 63);
+
+    struct UnitPos {
+        int n, oh, chunk;
+    };
+    auto unit_pos = [&](int u) {  // uniform
+        const int t = u / nchunks, c = u - t * nchunks;
+        const int row = j + t * n_ranks;
+        const int n = row / s.OH;
+        return UnitPos{n, row - n * s.OH, c};
+    };
+
+    u32x4 ra[kRowsPD][G::MAXT];
+    uint32_t rp[kRowsPD][G::MAXT];
+    auto load_unit = [&](int u, u32x4 (&a)[G::MAXT], uint32_t (&pv)[G::MAXT]) {
+        const UnitPos up = unit_pos(u);
+        const bool live = u < units;
+        const int ih0 = 2 * up.oh - 1;
+        const uint32_t base = (uint32_t)(((up.n * s.C_in + up.chunk * kChunk) * s.H + ih0) * s.W) * 2u;
+#pragma unroll
+        for (int q = 0; q < G::MAXT; ++q) {
+            const int ih = ih0 + tk_kh[q];
+            const bool ok = live && tk_valid[q] && (uint32_t)ih < (uint32_t)s.H;
+            const uint32_t off = base + tk_goff[q];
+            a[q] = buf_load16(xr, ok ? off : kOOB);
+            pv[q] = buf_load4(xr, ok && lane == 0 && !tk_first[q] ? off - 4u : kOOB);
+        }
+    };
+    // Split 8 input columns into the unit's three tap arrays (4 output
+    // pixels each) in LDS set `set`.
+    auto write_unit = [&](unsigned char *set, const u32x4 (&a)[G::MAXT], const uint32_t (&pv)[G::MAXT]) {
+#pragma unroll
+        for (int q = 0; q < G::MAXT; ++q) {
+            const u32x4 v = a[q];
+            const uint32_t e0 = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);
+            const uint32_t e1 = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
+            const uint32_t o0 = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
+            const uint32_t o1 = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
+            uint32_t prev = (uint32_t)__builtin_amdgcn_ds_bpermute(prev_lane_addr, (int)o1);
+            prev = lane == 0 ? pv[q] : prev;
+            prev = tk_first[q] ? 0u : prev;
+            if (!tk_valid[q]) continue;
+            unsigned char *dst = set + tk_lds[q];
+            *(u32x2 *)(dst) = u32x2{__builtin_amdgcn_perm(o0, prev, 0x05040302u), __builtin_amdgcn_alignbit(o1, o0, 16)};
+            *(u32x2 *)(dst + G::P) = u32x2{e0, e1};
+            *(u32x2 *)(dst + 2 * G::P) = u32x2{o0, o1};
+        }
+    };
+
+    // Weights of a unit: lane holds output channel co_lane and, for MFMA
+    // step ks (0..8), k = chunk*144 + 16*ks + 8*(lane>>5) .. +7 (the OIHW row
+    // of w restricted to the chunk's channels is contiguous).
+    const int co_lane = ct * kRowsTile + wave * 32 + (lane & 31);
+    u32x4 wf[2][9];
+    auto load_w = [&](int u, u32x4 (&f)[9]) {
+        const UnitPos up = unit_pos(u);
+        const bool ok = u < units && co_lane < s.C_out;
+        const uint32_t base = (uint32_t)(co_lane * s.K + up.chunk * kKRows + 8 * (lane >> 5)) * 2u;
+#pragma unroll
+        for (int ks = 0; ks < 9; ++ks) f[ks] = buf_load16(wr, ok ? base + 32u * ks : kOOB);
+    };
+
+    const float sc = co_lane < s.C_out ? scale[co_lane] : 0.f;
+    const float bi = co_lane < s.C_out ? bias[co_lane] : 0.f;
+
+    // A fragment geometry (32x32x16): lane l holds pixel l&31 of the block and
+    // k = 16*ks + 8*(l>>5) .. +7.  16-lane group G = l>>4 covers pixels
+    // 16*(G&1) .. +15 and k half G>>1; lane jj = l&15 of the group loads k-row
+    // 16*ks + 8*(G>>1) + (jj>>2) (+4 for the second read) at pixels
+    // 16*(G&1) + 4*(jj&3) .. +3.
+    const int grp = lane >> 4, jl = lane & 15;
+    const int tr_off = (8 * (grp >> 1) + (jl >> 2)) * G::P + 2 * (16 * (grp & 1) + 4 * (jl & 3));
+
+    f32x16 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
+
+    // Prologue: units 0..PD-1 in flight; unit 0 written to set 0; weights of
+    // unit 0 in wf[0].
+    rows_for<0, kRowsPD>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        load_unit(d, ra[d], rp[d]);
+    });
+    load_w(0, wf[0]);
+    write_unit(sets, ra[0], rp[0]);
+    load_unit(kRowsPD, ra[0], rp[0]);
+    __syncthreads();
+
+    // Unit u: write unit u+1 into set (u+1)%3 and request unit u+1+PD;
+    // request unit u+1's weights; barrier; then compute unit u from set u%3.
+    // The set written in unit u was last read in unit u-2, which every wave
+    // finished before the barrier of unit u-1.
+    auto run_unit = [&](int u, auto dc) {
+        constexpr int d = decltype(dc)::value;  // (u+1) % 2: register slot of unit u+1 (inputs and weights)
+        write_unit(sets + ((u + 1) % kSets) * G::SET, ra[d], rp[d]);
+        load_unit(u + 1 + kRowsPD, ra[d], rp[d]);
+        load_w(u + 1, wf[d]);
+        __syncthreads();
+        const unsigned char *set = sets + (u % kSets) * G::SET;
+        const u32x4(&wcurf)[9] = wf[1 - d];
+        // The fragments of step ks+1 are read while the NB matrix
+        // instructions of step ks run (two fragment sets).
+        bf16x8 af[2][NB];
+        auto read_step = [&](int ks, bf16x8 (&a)[NB]) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const unsigned char *p = set + tr_off + ks * 16 * G::P + 64 * b;
+                const u32x2 lo = rows_tr(p);
+                const u32x2 hi = rows_tr(p + 4 * G::P);
+                a[b] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+            }
+        };
+        read_step(0, af[0]);
+        rows_for<0, 9>([&](auto kc) {
+            constexpr int ks = decltype(kc)::value;
+            if constexpr (ks + 1 < 9) read_step(ks + 1, af[(ks + 1) & 1]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][b], __builtin_bit_cast(bf16x8, wcurf[ks]),
+                                                                 acc[b], 0, 0, 0);
+        });
+        const UnitPos up = unit_pos(u);
+        if (up.chunk != nchunks - 1) return;  // uniform
+        // Epilogue of output row (n, oh): lane holds channel co_lane, pixels
+        // 32b + 8*(i>>2) + 4*(lane>>5) + (i&3).
+        const uint32_t obase = (uint32_t)(((up.n * s.C_out + co_lane) * s.OH + up.oh) * s.OW) * 2u;
+        const bool cok = co_lane < s.C_out;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int px = 32 * b + 8 * q + 4 * (lane >> 5);
+                float o[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    o[r] = EPI == kFused ? bn_silu(acc[b][4 * q + r], sc, bi) : acc[b][4 * q + r];
+                const bool ok = cok && px < s.OW;
+                buf_store8(yr, ok ? obase + 2u * px : kOOB, u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
+        }
+    };
+    static_assert(kRowsPD == 2, "register slots alternate with unit parity");
+    for (int u0 = 0; u0 < units; u0 += 2) {
+        run_unit(u0, std::integral_constant<int, 1>{});
+        if (u0 + 1 < units) run_unit(u0 + 1, std::integral_constant<int, 0>{});
+    }
+}
+
+template <int NB, int EPI>
+hipError_t launch_rows_t(const Shape &s, const void *x, const void *w, const float *scale, const float *bias,
+                         void *y, hipStream_t st, int num_cu) {
+    const int co_tiles = (s.C_out + kRowsTile - 1) / kRowsTile;
+    const int rows_total = s.N * s.OH;
+    int n_ranks = (num_cu + co_tiles - 1) / co_tiles;
+    if (n_ranks > rows_total) n_ranks = rows_total;
+    const int ranks_per_xcd = (n_ranks + 7) / 8;
+    hipLaunchKernelGGL((rows_bf16<NB, EPI>), dim3(ranks_per_xcd * 8 * co_tiles), dim3(kRowsThreads), 0, st,
+                       (const uint16_t *)x, (const uint16_t *)w, scale, bias, (uint16_t *)y, s, co_tiles,
+                       ranks_per_xcd, n_ranks);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool rows_supports(const Shape &s, int dtype) {
+    return dtype == kDtypeBf16 && s.KH == 3 && s.KW == 3 && s.stride == 2 && s.pad == 1 && s.C_in % kChunk == 0 &&
+           s.C_in <= 64 && s.W % 8 == 0 && s.OW == s.W / 2 && s.OW % 4 == 0 && s.OW <= RowsGeo<5>::OWMAX &&
+           (uint64_t)s.N * s.C_in * s.H * s.W * 2 <= kMaxBufferBytes &&
+           (uint64_t)s.N * s.C_out * s.OHW * 2 <= kMaxBufferBytes;
+}
+
+bool rows_pointers_ok(const void *x, const void *w, const void *y) {
+    return (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) & 15) == 0;
+}
+
+hipError_t launch_rows(const Shape &s, int epi, const void *x, const void *w, const float *scale, const float *bias,
+                       void *y, hipStream_t st, int num_cu) {
+#define CBS_ROWS(NB_)                                                                                 \
+    if (s.OW <= RowsGeo<NB_>::OWMAX)                                                                  \
+        return epi == kFused ? launch_rows_t<NB_, kFused>(s, x, w, scale, bias, y, st, num_cu)        \
+                             : launch_rows_t<NB_, kConvOnly>(s, x, w, scale, bias, y, st, num_cu);
+    CBS_ROWS(1) CBS_ROWS(3) CBS_ROWS(5)
+#undef CBS_ROWS
+    return hipErrorInvalidValue;
+}
+
+}  // namespace cbs

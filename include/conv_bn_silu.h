@@ -74,7 +74,10 @@ enum {
     CBS_VARIANT_SCALAR = 5,      /* one output element per lane, no tiling; small shapes */
     CBS_VARIANT_GEMM_WINDOW32 = 6, /* as GEMM_WINDOW on 32x32x16 MFMA with larger tiles
                                       per wave: channel-heavy layers (bf16) */
-    CBS_VARIANT_COUNT_ = 7
+    CBS_VARIANT_ROWS = 7,        /* 3x3 stride-2 pad-1 layers with C_in a multiple of 16
+                                    up to 64 (OW <= 160): per-row tap arrays in LDS,
+                                    transposed fragment reads (bf16) */
+    CBS_VARIANT_COUNT_ = 8
 };
 
 typedef struct conv_bn_silu_handle *conv_bn_silu_t;

@@ -55,7 +55,7 @@ def test_bad_handles():
 def test_status_and_variant_names():
     assert B.status_string(0) == "ok"
     assert B.status_string(99) == "unknown"
-    assert [B.variant_name(v) for v in range(7)] == list(B.VARIANTS)
+    assert [B.variant_name(v) for v in range(8)] == list(B.VARIANTS)
     assert B.variant_name(-1) == "unknown"
 
 
@@ -150,7 +150,7 @@ def test_validate_rejects_beyond_int32():
 def test_select_variant_on_workloads():
     for wl in synth.WORKLOADS.values():
         v = B.select_variant(wl.N, wl.C_in, wl.H, wl.W, wl.C_out, wl.KH, wl.KW, wl.stride, wl.pad, wl.dtype)
-        assert v in range(1, 7)
+        assert v in range(1, 8)
         assert B.variant_supports(v, wl.N, wl.C_in, wl.H, wl.W, wl.C_out, wl.KH, wl.KW, wl.stride, wl.pad,
                                   wl.dtype)
     assert B.select_variant(1, 1, 2, 2, 1, 3, 3, 1, 0, 1) == -1

@@ -77,6 +77,13 @@ SWEEP = [
     (1, 128, 24, 24, 64, 3, 3, 2, 1),
     (3, 64, 36, 8, 48, 5, 5, 1, 2),
     (2, 32, 30, 28, 96, 3, 3, 1, 1),
+    # stride-2 downsampling layers for the strided-rows variant: one to four
+    # 16-channel chunks, a partial and a second output-channel tile, odd
+    # heights, each row-width class
+    (2, 16, 18, 24, 40, 3, 3, 2, 1),
+    (1, 64, 33, 64, 128, 3, 3, 2, 1),
+    (3, 32, 20, 320, 136, 3, 3, 2, 1),
+    (2, 48, 12, 96, 64, 3, 3, 2, 1),
 ]
 
 
