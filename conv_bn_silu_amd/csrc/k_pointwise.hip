@@ -27,9 +27,10 @@
 //    pixels x 2 octets that a wave reads at once hit distinct banks.  (On
 //    gfx950 a transposed ds_read_b64_tr_b16 moves about a quarter of the
 //    bytes per cycle of a plain 16-byte read, so the transposition is done
-//    in registers while staging instead: a task loads 8 channels x 8 pixels,
-//    16 bytes per channel, and writes 8 records' octets.)
-//  * Two chunks of x are in flight in registers while one is computed.
+//    in registers while staging instead: a task loads 2 channels x 8 pixels,
+//    16 bytes per channel, and writes the pair into 8 pixels' records.)
+//  * Two chunks of x are in flight in registers while one is computed (four
+//    measured no faster: the steady state is at the mixed read/write rate).
 //  * The epilogue (folded BN, SiLU, bf16 rounding) runs on the accumulators;
 //    each wave stages its 32-channel output tile in LDS and writes y in whole
 //    128-byte rows, 16 bytes per lane.
@@ -85,9 +86,13 @@ __global__ __launch_bounds__(kThreadsPw, 1) void pointwise_bf16(
     int n_ranks) {
     constexpr int KP = KS * 16;                        // channels held in LDS (zero beyond C_in)
     constexpr int NKB = (KP + 31) / 32;                // 32-channel record blocks
-    constexpr int KBB = CP * 64;                       // bytes per record block of a chunk
-    constexpr int NTASK = (KP / 8) * (CP / 8);         // staging tasks: 8 channels x 8 pixels
-    static_assert(NTASK <= kThreadsPw, "one staging task per thread at most");
+    // Bytes per record block of a chunk, padded by one record so that the
+    // blocks start in different banks (the staging writes of one instruction
+    // cover several blocks).
+    constexpr int KBB = CP * 64 + 64;
+    constexpr int NPAIR = KP / 2;                      // channel pairs
+    constexpr int NTASK = NPAIR * (CP / 8);            // staging tasks: 2 channels x 8 pixels
+    constexpr int TPT = (NTASK + kThreadsPw - 1) / kThreadsPw;  // tasks per thread
     constexpr int MB = CP / 32;                        // 32-pixel blocks per chunk
     constexpr int OROW = CP + 8;                       // output staging: elements per channel row
     // One LDS area, used first for the workgroup's weight tile (kTileCo
@@ -138,36 +143,41 @@ __global__ __launch_bounds__(kThreadsPw, 1) void pointwise_bf16(
     float sc, bi, sn, bn;
 
 
-    // Staging task t < NTASK: channel octet o = t / (CP/8) (channels 8o ..
-    // 8o+7), 8-pixel piece t % (CP/8).  A piece outside the workgroup's
-    // range, a channel past C_in, or a chunk past the last, gets an
-    // out-of-range offset: the load returns zeros and costs no memory
-    // traffic.
-    const bool stager = tid < NTASK;
-    const int st_o = tid / (CP / 8), st_piece = tid % (CP / 8);
-    auto load_chunk = [&](int c, u32x4 (&r)[8]) {
+    // Staging task t < NTASK (t = tid + q*threads): channel pair cp = t %
+    // NPAIR (channels 2cp, 2cp+1), 8-pixel piece t / NPAIR; two 16-byte
+    // loads, and per pixel one 4-byte LDS write of the pair into the pixel's
+    // record.  A piece outside the range, a channel past C_in, or a chunk past
+    // the last, gets an out-of-range offset: the load returns zeros and costs
+    // no memory traffic.
+    auto load_chunk = [&](int c, u32x4 (&r)[TPT][2]) {
         const PixPos c0 = chunk_pos(c);
         const int mc = (j + c * n_ranks) * CP;
-        const PixPos pp = advance(c0, 8 * st_piece, hw);
-        const bool ok = stager && c < n_chunks && mc + 8 * st_piece < s.M;
-        const uint32_t off0 = (uint32_t)((pp.n * s.C_in + 8 * st_o) * hw + pp.p) * 2u;
 #pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8)
-            r[c8] = buf_load16(xr, ok && 8 * st_o + c8 < s.C_in ? off0 + (uint32_t)(c8 * hw) * 2u : kOOB);
+        for (int q = 0; q < TPT; ++q) {
+            const int t = tid + q * kThreadsPw;
+            const int cp = t % NPAIR, piece = t / NPAIR;
+            const PixPos pp = advance(c0, 8 * piece, hw);
+            const bool ok = t < NTASK && c < n_chunks && mc + 8 * piece < s.M && 2 * cp < s.C_in;
+            const uint32_t off0 = (uint32_t)((pp.n * s.C_in + 2 * cp) * hw + pp.p) * 2u;
+            r[q][0] = buf_load16(xr, ok ? off0 : kOOB);
+            r[q][1] = buf_load16(xr, ok ? off0 + (uint32_t)hw * 2u : kOOB);
+        }
     };
-    // Transpose a task's 8 channels x 8 pixels and write the pixels' octets.
-    auto store_chunk = [&](int buf, const u32x4 (&r)[8]) {
-        if (!stager) return;
-        unsigned char *blk = &xs[buf][(st_o >> 2) * KBB];
+    auto store_chunk = [&](int buf, const u32x4 (&r)[TPT][2]) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            u32x4 v;
+        for (int q = 0; q < TPT; ++q) {
+            const int t = tid + q * kThreadsPw;
+            if (TPT * kThreadsPw != NTASK && t >= NTASK) continue;
+            const int cp = t % NPAIR, piece = t / NPAIR;
+            unsigned char *blk = &xs[buf][(cp >> 4) * KBB] + (cp & 3) * 4;  // block, word in octet
+            const int oct = (cp >> 2) & 3;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t lo = r[2 * d][p >> 1], hi = r[2 * d + 1][p >> 1];
-                v[d] = (p & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u) : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            for (int p = 0; p < 8; ++p) {
+                const uint32_t lo = r[q][0][p >> 1], hi = r[q][1][p >> 1];
+                const uint32_t v = (p & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                                           : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                *(uint32_t *)(blk + rec_off(8 * piece + p, oct)) = v;
             }
-            *(u32x4 *)(blk + rec_off(8 * st_piece + p, st_o & 3)) = v;
         }
     };
 
@@ -276,7 +286,7 @@ __global__ __launch_bounds__(kThreadsPw, 1) void pointwise_bf16(
                 0);
         }
     }
-    u32x4 r[PD][8];
+    u32x4 r[PD][TPT][2];
 #pragma unroll
     for (int d = 0; d < PD; ++d) load_chunk(d, r[d]);
 
