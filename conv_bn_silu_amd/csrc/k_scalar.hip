@@ -5,7 +5,8 @@
 //
 // The scalar kernel has no setup: each lane walks the whole reduction for one
 // output in the order ci, kh, kw with fp32 fused multiply-adds and applies
-// the epilogue to its own result.  Lanes run along ow, so loads of x and the
+// the epilogue to its own result (a 3x3 form with unrolled, branch-free taps
+// serves the common filter).  Lanes run along ow, so loads of x and the
 // store of y are coalesced along rows.
 #include "cbs_device.h"
 #include "cbs_launch.h"
@@ -46,6 +47,48 @@ __global__ __launch_bounds__(kThreads) void conv_scalar(const T *__restrict__ x,
     }
 }
 
+// The same operation for 3x3 filters with the taps unrolled and the padding
+// applied by masking rather than branching (an out-of-image tap loads from a
+// clamped in-image address and is multiplied by zero), so that a lane's loads
+// are independent of each other and issue back to back; the channel loop is
+// unrolled by four for the same reason.  Same summation order as above.
+template <typename T, int EPI>
+__global__ __launch_bounds__(kThreads) void conv_scalar3x3(const T *__restrict__ x, const T *__restrict__ w,
+                                                           const float *__restrict__ scale,
+                                                           const float *__restrict__ bias, T *__restrict__ y,
+                                                           Shape s) {
+    const int total = s.N * s.C_out * s.OHW;
+    for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
+        const int ow = idx % s.OW;
+        const int oh = (idx / s.OW) % s.OH;
+        const int co = (idx / s.OHW) % s.C_out;
+        const int n = idx / (s.OHW * s.C_out);
+        const int ih0 = oh * s.stride - s.pad, iw0 = ow * s.stride - s.pad;
+        int off[9];
+        float msk[9];
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw) {
+                const int ih = ih0 + kh, iw = iw0 + kw;
+                const bool in = (unsigned)ih < (unsigned)s.H && (unsigned)iw < (unsigned)s.W;
+                off[kh * 3 + kw] = in ? ih * s.W + iw : 0;
+                msk[kh * 3 + kw] = in ? 1.f : 0.f;
+            }
+        const T *xn = x + (size_t)n * s.C_in * s.HW;
+        const T *wc = w + (size_t)co * s.K;
+        float acc = 0.f;
+#pragma unroll 4
+        for (int ci = 0; ci < s.C_in; ++ci) {
+            const T *xc = xn + ci * s.HW;
+#pragma unroll
+            for (int t = 0; t < 9; ++t)
+                acc = __builtin_fmaf(Elem<T>::load(xc + off[t]) * msk[t], Elem<T>::load(wc + ci * 9 + t), acc);
+        }
+        Elem<T>::store(y + idx, EPI == kFused ? bn_silu(acc, scale[co], bias[co]) : acc);
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bn_pass(const T *__restrict__ t1, const float *__restrict__ scale,
                                                     const float *__restrict__ bias, T *__restrict__ t2,
@@ -77,17 +120,22 @@ bool scalar_supports(const Shape &, int) { return true; }
 hipError_t launch_scalar(const Shape &s, int dtype, int epi, const void *x, const void *w,
                          const float *scale, const float *bias, void *y, hipStream_t st) {
     const dim3 grid(grid_for(s.N * s.C_out * s.OHW)), block(kThreads);
+    const bool k3 = s.KH == 3 && s.KW == 3;
     if (dtype == kDtypeBf16) {
         auto xx = (const uint16_t *)x;
         auto ww = (const uint16_t *)w;
         auto yy = (uint16_t *)y;
-        if (epi == kFused) hipLaunchKernelGGL((conv_scalar<uint16_t, kFused>), grid, block, 0, st, xx, ww, scale, bias, yy, s);
+        if (k3 && epi == kFused) hipLaunchKernelGGL((conv_scalar3x3<uint16_t, kFused>), grid, block, 0, st, xx, ww, scale, bias, yy, s);
+        else if (k3) hipLaunchKernelGGL((conv_scalar3x3<uint16_t, kConvOnly>), grid, block, 0, st, xx, ww, scale, bias, yy, s);
+        else if (epi == kFused) hipLaunchKernelGGL((conv_scalar<uint16_t, kFused>), grid, block, 0, st, xx, ww, scale, bias, yy, s);
         else hipLaunchKernelGGL((conv_scalar<uint16_t, kConvOnly>), grid, block, 0, st, xx, ww, scale, bias, yy, s);
     } else {
         auto xx = (const float *)x;
         auto ww = (const float *)w;
         auto yy = (float *)y;
-        if (epi == kFused) hipLaunchKernelGGL((conv_scalar<float, kFused>), grid, block, 0, st, xx, ww, scale, bias, yy, s);
+        if (k3 && epi == kFused) hipLaunchKernelGGL((conv_scalar3x3<float, kFused>), grid, block, 0, st, xx, ww, scale, bias, yy, s);
+        else if (k3) hipLaunchKernelGGL((conv_scalar3x3<float, kConvOnly>), grid, block, 0, st, xx, ww, scale, bias, yy, s);
+        else if (epi == kFused) hipLaunchKernelGGL((conv_scalar<float, kFused>), grid, block, 0, st, xx, ww, scale, bias, yy, s);
         else hipLaunchKernelGGL((conv_scalar<float, kConvOnly>), grid, block, 0, st, xx, ww, scale, bias, yy, s);
     }
     return hipGetLastError();
