@@ -1,16 +1,16 @@
-// k_window32.hip -- implicit-GEMM convolution on v_mfma_f32_32x32x16_bf16
+// k_window32.hip -- implicit-GEMM 3x3 convolution on v_mfma_f32_32x32x16_bf16
 // for the compute-bound layers (many channels, small images): the input
 // window of a tile is staged in LDS once per 32-channel block and reused by
-// every kernel tap, as in the 16x16 window kernel, but each wave holds a
-// 7 x 2 grid of 32x32 accumulators so that every fragment read from LDS
-// feeds several matrix instructions ("Fusing an Epilogue", section "Three
-// kernels for one operation": the GEMM kernel has the best arithmetic
-// intensity).
+// all nine kernel taps, as in the 16x16 window kernel, but each wave holds a
+// column of 7 32x32 accumulators so that every weight fragment read from LDS
+// feeds 7 matrix instructions ("Fusing an Epilogue", section "Three kernels
+// for one operation": the GEMM kernel has the best arithmetic intensity).
 //
-// Workgroup: 4 waves (one per SIMD) as 2 (pixels) x 2 (channels); tile =
+// Workgroup: 8 waves (two per SIMD, so that one wave's staging and waits
+// hide behind the other's matrix work) as 2 (pixels) x 4 (channels); tile =
 // TH x TW output pixels of one image x 128 output channels; wave (wm, wn)
 // owns pixel blocks wm*MB .. wm*MB+MB-1 (32 pixels each, pixel p of the tile
-// = row p / TW, column p mod TW) and output channels 64*wn .. +63.
+// = row p / TW, column p mod TW) and output channels 32*wn .. +31.
 //
 // Reduction order: channel block (32 channels), then the tap (a "unit"),
 // then two 16-channel halves.  LDS holds two window buffers (this channel
@@ -23,14 +23,15 @@
 // lane -- is one ds_read_b128 whose per-tap part of the address is a
 // uniform offset.
 //
-// Staging is through registers and runs well ahead of use, so that the
-// load latency hides behind the matrix work of one workgroup per CU: a
-// tap's weights (128 channels x 64 bytes, 2 x 16 bytes per thread) are
-// requested three units ahead (a ring of three register sets; the unit loop
-// is unrolled by three), and the next channel block's whole window (up to 3
-// parts of 256 tasks, each task 8 channels x VEC columns, transposed with
-// byte permutes) is requested at the start of a block and written at its
-// end.
+// Staging is through registers and runs well ahead of use: a tap's weights
+// (128 channels x 64 bytes, 16 bytes per thread) are requested three units
+// ahead (a ring of three register sets), and the next channel block's whole
+// window (up to 2 parts of 512 tasks, each task 8 channels x VEC columns,
+// transposed with byte permutes) is requested at the start of a block and
+// written at its end.  The nine taps are unrolled with the stride fixed at
+// compile time, and blocks advance by counters, so that a unit costs no
+// integer division: the scalar unit, shared by both waves of a SIMD, would
+// otherwise issue more instructions per unit than the matrix core runs.
 #include <type_traits>
 
 #include "cbs_device.h"
@@ -40,13 +41,13 @@ namespace cbs {
 
 namespace {
 
-constexpr int kThreads32 = 256;
+constexpr int kThreads32 = 512;
 constexpr int kBN32 = 128;            // output channels per tile
 constexpr int kCK32 = 32;             // input channels per block
 constexpr int kRec = 80;              // bytes per record (64 data + 16 padding)
 constexpr int kFpBytes32 = 41 * 1024; // one window buffer
 constexpr int kWTB = kBN32 * kRec;    // one weight buffer: one tap x 128 records
-constexpr int kParts = 3;             // window parts (256 tasks each) at most
+constexpr int kParts = 2;             // window parts (512 tasks each) at most
 
 // Calls f(integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, typename F>
@@ -71,138 +72,117 @@ template <> struct XV32<4> {
     __device__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) { return buf_load8(r, off); }
 };
 
-// MB: 32-pixel blocks per wave; VEC: input columns per staging load.
-template <int MB, int VEC, int EPI>
+// MB: 32-pixel blocks per wave; VEC: input columns per staging load (8 or
+// 4); S: stride (1 or 2).
+template <int MB, int VEC, int S, int EPI>
 __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wp, const float *__restrict__ scale,
     const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, WinGeo g) {
     __shared__ __attribute__((aligned(16))) unsigned char fps[2][kFpBytes32];
     __shared__ __attribute__((aligned(16))) unsigned char wbs[2][kWTB];
     typedef typename XV32<VEC>::T XT;
+    constexpr int kT = 9;  // taps
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int l32 = lane & 31, hi = lane >> 5;
 
     const int t_begin = (int)blockIdx.x * g.tiles_per_wg;
     const int t_end = min(t_begin + g.tiles_per_wg, g.n_tiles);
     if (t_begin >= t_end) return;  // uniform
-    const int steps = (t_end - t_begin) * g.n_chunks;  // (tile, channel block) pairs
-    const int upt = g.n_chunks * s.T;                  // units (channel block, tap) per tile
-    const int upt3 = (upt + 2) / 3 * 3;                // padded to a multiple of 3 (tail units idle)
-    const int units = (t_end - t_begin) * upt3;
+    const int n_steps = (t_end - t_begin) * g.n_chunks;  // (tile, channel block) pairs
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.C_in * s.HW * 2u);
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)s.C_out * g.n_chunks * s.T * 64u);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)s.C_out * g.n_chunks * kT * 64u);
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)s.N * s.C_out * s.OHW * 2u);
 
-    struct Tile {
-        int n, oh0, ow0, co0;
+    // A block: one 32-channel slice of one tile.
+    struct Blk {
+        int tile, n, oh0, ow0, co0, ck;
+        bool live;
     };
-    auto tile_of = [&](int t) {
-        Tile r;
+    auto block_at = [&](int tile, int ck, bool live) {
+        Blk r;
+        const int t = live ? tile : t_begin;
         const int ct = t % g.co_tiles;
         int q = t / g.co_tiles;
         const int tw = q % g.tiles_w;
         q /= g.tiles_w;
+        r.tile = tile;
         r.oh0 = (q % g.tiles_h) * g.TH;
         r.n = q / g.tiles_h;
         r.ow0 = tw * g.TW;
         r.co0 = ct * kBN32;
+        r.ck = ck;
+        r.live = live;
         return r;
     };
-    // Unit u -> (step, tap); a tile's padding units have none.
-    struct Unit {
-        int step, tap;
-        bool real;
-    };
-    auto unit_of = [&](int u) {
-        const int tl = u / upt3, k = u - tl * upt3;
-        Unit r;
-        r.real = u < units && k < upt;
-        const int kk = k < upt ? k : upt - 1;
-        r.step = tl * g.n_chunks + kk / s.T;
-        r.tap = kk % s.T;
-        return r;
+    auto next_of = [&](const Blk &b) {
+        if (b.ck + 1 < g.n_chunks) {
+            Blk r = b;
+            r.ck = b.ck + 1;
+            return r;
+        }
+        return block_at(b.tile + 1, 0, b.live && b.tile + 1 < t_end);
     };
 
     // ---- window staging ----------------------------------------------------
-    // Task t (part f = t / 256): octet o = t&3, row parity (t>>2)&1, column
-    // group (t>>3) % ncg, row pair (t>>3) / ncg.
+    // Task t = tid + 512 f: octet o = t&3, row parity (t>>2)&1, column group
+    // (t>>3) % ncg, row pair (t>>3) / ncg; fixed per thread, so computed once.
     const int nparts = (((g.FR + 1) / 2) * g.ncg * 8 + kThreads32 - 1) / kThreads32;  // <= kParts
-    auto fp_load = [&](int step, int f, XT (&reg)[8]) {
-        const int tile = t_begin + step / g.n_chunks;
-        const int ck = step % g.n_chunks;
-        const bool live = step < steps && f < nparts;
-        const Tile tl = tile_of(live ? tile : t_begin);
-        const int iw_lo = tl.ow0 * s.stride - s.pad;
-        const int g0 = (iw_lo >= 0 ? iw_lo / VEC : -((-iw_lo + VEC - 1) / VEC)) * VEC;
-        const int t = tid + f * kThreads32;
-        const int rest = t >> 3, o = t & 3;
-        const int cg = rest % g.ncg, r = 2 * (rest / g.ncg) + ((t >> 2) & 1);
-        const int ih = tl.oh0 * s.stride - s.pad + r;
-        const int iw0 = g0 + cg * VEC;
-        const bool ok = live && r < g.FR && (unsigned)ih < (unsigned)s.H && iw0 >= 0 && iw0 < s.W &&
-                        iw0 + VEC - 1 >= iw_lo && iw0 <= iw_lo + g.FC - 1;
-        const uint32_t off0 = (uint32_t)(((tl.n * s.C_in + ck * kCK32 + 8 * o) * s.H + ih) * s.W + iw0) * 2u;
+    int tk_o[kParts], tk_cg[kParts], tk_r[kParts];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int ci = ck * kCK32 + 8 * o + c;
-            reg[c] = XV32<VEC>::load(xr, (ok && ci < s.C_in) ? off0 + (uint32_t)(c * s.HW) * 2u : kOOB);
-        }
-    };
-    auto fp_store = [&](int step, int f, unsigned char *fp, const XT (&reg)[8]) {
-        if (f >= nparts) return;  // uniform
-        const int tile = t_begin + step / g.n_chunks;
-        const Tile tl = tile_of(step < steps ? tile : t_begin);
-        const int iw_lo = tl.ow0 * s.stride - s.pad;
-        const int g0 = (iw_lo >= 0 ? iw_lo / VEC : -((-iw_lo + VEC - 1) / VEC)) * VEC;
+    for (int f = 0; f < kParts; ++f) {
         const int t = tid + f * kThreads32;
-        const int rest = t >> 3, o = t & 3;
-        const int cg = rest % g.ncg, r = 2 * (rest / g.ncg) + ((t >> 2) & 1);
+        const int rest = t >> 3;
+        tk_o[f] = t & 3;
+        tk_cg[f] = rest % g.ncg;
+        tk_r[f] = 2 * (rest / g.ncg) + ((t >> 2) & 1);
+        if (f >= nparts) tk_r[f] = g.FR;  // no rows: idle task
+    }
+    auto fp_load = [&](const Blk &b, int f, XT (&reg)[8]) {
+        const int iw_lo = b.ow0 * S - s.pad;
+        const int g0 = iw_lo & ~(VEC - 1);  // floor to a multiple of VEC
+        const int r = tk_r[f];
+        const int ih = b.oh0 * S - s.pad + r;
+        const int iw0 = g0 + tk_cg[f] * VEC;
+        const bool ok = b.live && r < g.FR && (unsigned)ih < (unsigned)s.H && iw0 >= 0 && iw0 < s.W &&
+                        iw0 + VEC - 1 >= iw_lo && iw0 <= iw_lo + g.FC - 1;
+        const int ci0 = b.ck * kCK32 + 8 * tk_o[f];
+        const uint32_t off0 = (uint32_t)(((b.n * s.C_in + ci0) * s.H + ih) * s.W + iw0) * 2u;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            reg[c] = XV32<VEC>::load(xr, (ok && ci0 + c < s.C_in) ? off0 + (uint32_t)(c * s.HW) * 2u : kOOB);
+    };
+    auto fp_store = [&](const Blk &b, int f, unsigned char *fp, const XT (&reg)[8]) {
+        const int r = tk_r[f];
         if (r >= g.FR) return;
-        const int c0 = g0 + cg * VEC - iw_lo;  // window column of the group's first element (> -VEC)
-        const int c0p = c0 + VEC * s.stride;
-        int quo = c0p / s.stride - VEC, rem = c0p - (c0p / s.stride) * s.stride;
+        const int iw_lo = b.ow0 * S - s.pad;
+        const int g0 = iw_lo & ~(VEC - 1);
+        const int c0 = g0 + tk_cg[f] * VEC - iw_lo;  // window column of the group's first element (> -VEC)
+        unsigned char *row = fp + (r * g.FCP) * kRec + tk_o[f] * 16;
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
             const int c = c0 + j;
-            const int pos = r * g.FCP + rem * g.CS + quo;
-            if (++rem == s.stride) {
-                rem = 0;
-                ++quo;
-            }
             if (c < 0 || c >= g.FC) continue;
+            // window column c sits at (c mod S) * CS + c / S: the columns of
+            // one phase are contiguous, so a tap's columns are consecutive
+            const int pos = S == 1 ? c : (c & 1) * g.CS + (c >> 1);
             u32x4 v;
 #pragma unroll
             for (int d = 0; d < 4; ++d) v[d] = pair16(reg[2 * d][j >> 1], reg[2 * d + 1][j >> 1], j & 1);
-            *(u32x4 *)(fp + pos * kRec + o * 16) = v;
+            *(u32x4 *)(row + pos * kRec) = v;
         }
     };
 
-    // ---- weight staging: one tap x 128 channels x 4 octets; thread piece q
-    // (0, 1): channel (q*256 + tid) >> 2, octet tid & 3 ----------------------
-    auto w_load = [&](int u, u32x4 (&reg)[2]) {
-        const Unit un = unit_of(u);
-        const int tile = t_begin + un.step / g.n_chunks;
-        const int ck = un.step % g.n_chunks;
-        const int co0 = (tile % g.co_tiles) * kBN32;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int p = q * kThreads32 + tid;
-            const int co = co0 + (p >> 2);
-            const bool ok = un.real && co < s.C_out;
-            reg[q] = buf_load16(wr, ok ? (uint32_t)(((co * g.n_chunks + ck) * s.T + un.tap) * 64 + (p & 3) * 16)
-                                       : kOOB);
-        }
+    // ---- weight staging: one tap x 128 channels x 4 octets; thread: channel
+    // tid >> 2, octet tid & 3 --------------------------------------------------
+    const uint32_t w_lane = (uint32_t)((tid >> 2) * g.n_chunks * kT * 64 + (tid & 3) * 16);
+    auto w_load = [&](const Blk &b, int tap) {
+        const bool ok = b.live && b.co0 + (tid >> 2) < s.C_out;
+        return buf_load16(wr, ok ? (uint32_t)((b.co0 * g.n_chunks + b.ck) * kT + tap) * 64u + w_lane : kOOB);
     };
-    auto w_store = [&](unsigned char *wb, const u32x4 (&reg)[2]) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int p = q * kThreads32 + tid;
-            *(u32x4 *)(wb + (p >> 2) * kRec + (p & 3) * 16) = reg[q];
-        }
-    };
+    unsigned char *const w_dst = &wbs[0][0] + (tid >> 2) * kRec + (tid & 3) * 16;
 
     // ---- per-lane fragment geometry ----------------------------------------
     const int tile_px = g.TH * g.TW;
@@ -211,65 +191,63 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     for (int b = 0; b < MB; ++b) {
         const int px = (wm * MB + b) * 32 + l32;
         const int i = px / g.TW, j = px - (px / g.TW) * g.TW;
-        abase[b] = (uint32_t)((px < tile_px ? i * s.stride * g.FCP + j : 0) * kRec + hi * 16);
+        abase[b] = (uint32_t)((px < tile_px ? i * S * g.FCP + j : 0) * kRec + hi * 16);
     }
-    uint32_t bbase[2];  // weight record of this lane, octet hi
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) bbase[cb] = (uint32_t)((wn * 64 + 32 * cb + l32) * kRec + hi * 16);
+    const uint32_t bbase = (uint32_t)((wn * 32 + l32) * kRec + hi * 16);  // weight record of this lane, octet hi
+    const int fcp_b = g.FCP * kRec, cs_b = g.CS * kRec;
 
-    f32x16 acc[MB][2];
+    f32x16 acc[MB];
 #pragma unroll
     for (int b = 0; b < MB; ++b)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[b][cb][e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
 
-    // Prologue: window of step 0 and weights of unit 0 into buffers 0;
-    // weights of units 1 and 2 in flight in ring slots 1 and 2.
+    // Prologue: the window of the first block and the weights of its tap 0
+    // into buffers 0; taps 1 and 2 in flight in ring slots 1 and 2.
+    Blk cur = block_at(t_begin, 0, true);
+    Blk nxt = next_of(cur);
     XT fpr[kParts][8];
-    u32x4 wreg[3][2];
-    w_load(0, wreg[0]);
+    u32x4 wreg[3];
+    wreg[0] = w_load(cur, 0);
     static_for<0, kParts>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
-        fp_load(0, f, fpr[f]);
+        fp_load(cur, f, fpr[f]);
     });
-    w_load(1, wreg[1]);
-    w_load(2, wreg[2]);
+    wreg[1] = w_load(cur, 1);
+    wreg[2] = w_load(cur, 2);
     static_for<0, kParts>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
-        fp_store(0, f, fps[0], fpr[f]);
+        fp_store(cur, f, fps[0], fpr[f]);
     });
-    w_store(wbs[0], wreg[0]);
+    *(u32x4 *)w_dst = wreg[0];
     __syncthreads();
 
-    // Unit u (ring slot u mod 3): request unit u+3's weights; at a block's
-    // first tap request the next block's window; the two half-steps (the
-    // second's fragments read while the first's 2*MB matrix instructions
-    // run); write unit u+1's weights, and after a block's last tap the next
-    // window; barrier.
-    bf16x8 fa[2][MB], fb[2][2];
-    auto run_unit = [&](int u, auto slot_c) {
-        constexpr int sl = decltype(slot_c)::value;
-        const Unit un = unit_of(u);
-        w_load(u + 3, wreg[sl]);
-        const bool first = un.real && un.tap == 0;
-        const bool last = un.real && un.tap == s.T - 1;
-        if (first) {
-            static_for<0, kParts>([&](auto fc) {
-                constexpr int f = decltype(fc)::value;
-                fp_load(un.step + 1, f, fpr[f]);
-            });
-        }
-        if (un.real) {
-            const unsigned char *fp = fps[un.step & 1];
-            const unsigned char *wb = wbs[u & 1];
-            const int kh = un.tap / s.KW, kw = un.tap - kh * s.KW;
-            const int toff = (kh * g.FCP + (kw % s.stride) * g.CS + kw / s.stride) * kRec;
+    // Unit (block, tap), ring slot tap mod 3, weight buffer (unit index) mod 2
+    // = (step + tap) mod 2 as nine is odd: request the weights three units
+    // ahead; at tap 0 request the next block's window; the two half-steps
+    // (the second's fragments read while the first's MB matrix instructions
+    // run); write the next unit's weights, and after tap 8 the next window;
+    // barrier.
+    bf16x8 fa[2][MB], fb[2];
+    for (int step = 0; step < n_steps; ++step) {
+        const unsigned char *fp = fps[step & 1];
+        static_for<0, kT>([&](auto tc) {
+            constexpr int tap = decltype(tc)::value;
+            constexpr int sl = tap % 3;
+            wreg[sl] = tap + 3 < kT ? w_load(cur, tap + 3) : w_load(nxt, tap + 3 - kT);
+            if (tap == 0) {
+                static_for<0, kParts>([&](auto fc) {
+                    constexpr int f = decltype(fc)::value;
+                    fp_load(nxt, f, fpr[f]);
+                });
+            }
+            const int wsel = (step + tap) & 1;
+            const unsigned char *wb = &wbs[0][0] + wsel * kWTB;
+            constexpr int kh = tap / 3, kw = tap % 3;
+            const int toff = kh * fcp_b + (kw % S) * cs_b + (kw / S) * kRec;
             static_for<0, 2>([&](auto hc) {
                 constexpr int h = decltype(hc)::value;
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) fb[h][cb] = *(const bf16x8 *)(wb + bbase[cb] + 32 * h);
+                fb[h] = *(const bf16x8 *)(wb + bbase + 32 * h);
 #pragma unroll
                 for (int b = 0; b < MB; ++b) fa[h][b] = *(const bf16x8 *)(fp + abase[b] + toff + 32 * h);
             });
@@ -277,73 +255,55 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
                 constexpr int h = decltype(hc)::value;
 #pragma unroll
                 for (int b = 0; b < MB; ++b)
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb)
-                        acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[h][b], fb[h][cb], acc[b][cb], 0, 0, 0);
+                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[h][b], fb[h], acc[b], 0, 0, 0);
             });
-        }
-        w_store(wbs[(u + 1) & 1], wreg[(sl + 1) % 3]);
-        if (last) {
-            static_for<0, kParts>([&](auto fc) {
-                constexpr int f = decltype(fc)::value;
-                fp_store(un.step + 1, f, fps[(un.step + 1) & 1], fpr[f]);
-            });
-        }
-        __syncthreads();
-    };
+            *(u32x4 *)(w_dst + (wsel ^ 1) * kWTB) = wreg[(sl + 1) % 3];
+            if (tap == kT - 1) {
+                static_for<0, kParts>([&](auto fc) {
+                    constexpr int f = decltype(fc)::value;
+                    fp_store(nxt, f, fps[(step + 1) & 1], fpr[f]);
+                });
+            }
+            __syncthreads();
+        });
 
-    for (int tile = t_begin; tile < t_end; ++tile) {
-        const int u0 = (tile - t_begin) * upt3;
-        for (int k = 0; k < upt3; k += 3) {
-            run_unit(u0 + k, std::integral_constant<int, 0>{});
-            run_unit(u0 + k + 1, std::integral_constant<int, 1>{});
-            run_unit(u0 + k + 2, std::integral_constant<int, 2>{});
-        }
-
-        // ---- epilogue for the finished tile --------------------------------
-        // (The tile width is passed through an empty asm so that the pixel
-        // coordinates below are computed here, not hoisted out of the loop
-        // into registers the reduction needs.)
-        int tw_e = g.TW;
-        asm volatile("" : "+s"(tw_e));
-        const Tile tl = tile_of(tile);
-        float sc[2], bi[2];
+        if (cur.ck == g.n_chunks - 1) {
+            // ---- epilogue for the finished tile ----------------------------
+            // (The tile width is passed through an empty asm so that the pixel
+            // coordinates below are computed here, not hoisted out of the loop
+            // into registers the reduction needs.)
+            int tw_e = g.TW;
+            asm volatile("" : "+s"(tw_e));
+            const int co = cur.co0 + wn * 32 + l32;
+            const float sc = co < s.C_out ? scale[co] : 0.f;
+            const float bi = co < s.C_out ? bias[co] : 0.f;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            const int co = tl.co0 + wn * 64 + 32 * cb + l32;
-            sc[cb] = co < s.C_out ? scale[co] : 0.f;
-            bi[cb] = co < s.C_out ? bias[co] : 0.f;
-        }
+            for (int b = 0; b < MB; ++b) {
 #pragma unroll
-        for (int b = 0; b < MB; ++b) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int px = (wm * MB + b) * 32 + 8 * q + 4 * hi;
-                const int i = px / tw_e, j = px - i * tw_e;
-                const int oh = tl.oh0 + i, ow = tl.ow0 + j;
-                const bool pok = px < tile_px && oh < s.OH && ow < s.OW;
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    const int co = tl.co0 + wn * 64 + 32 * cb + l32;
-                    const bool ok = pok && co < s.C_out;
+                for (int q = 0; q < 4; ++q) {
+                    const int px = (wm * MB + b) * 32 + 8 * q + 4 * hi;
+                    const int i = px / tw_e, j = px - i * tw_e;
+                    const int oh = cur.oh0 + i, ow = cur.ow0 + j;
+                    const bool ok = px < tile_px && oh < s.OH && ow < s.OW && co < s.C_out;
                     u32x2 o;
-                    const float v0 = acc[b][cb][4 * q], v1 = acc[b][cb][4 * q + 1];
-                    const float v2 = acc[b][cb][4 * q + 2], v3 = acc[b][cb][4 * q + 3];
+                    const float v0 = acc[b][4 * q], v1 = acc[b][4 * q + 1];
+                    const float v2 = acc[b][4 * q + 2], v3 = acc[b][4 * q + 3];
                     if (EPI == kFused) {
-                        o.x = pack_bf16x2(bn_silu(v0, sc[cb], bi[cb]), bn_silu(v1, sc[cb], bi[cb]));
-                        o.y = pack_bf16x2(bn_silu(v2, sc[cb], bi[cb]), bn_silu(v3, sc[cb], bi[cb]));
+                        o.x = pack_bf16x2(bn_silu(v0, sc, bi), bn_silu(v1, sc, bi));
+                        o.y = pack_bf16x2(bn_silu(v2, sc, bi), bn_silu(v3, sc, bi));
                     } else {
                         o.x = pack_bf16x2(v0, v1);
                         o.y = pack_bf16x2(v2, v3);
                     }
-                    buf_store8(yr, ok ? (uint32_t)(((tl.n * s.C_out + co) * s.OH + oh) * s.OW + ow) * 2u : kOOB, o);
+                    buf_store8(yr, ok ? (uint32_t)(((cur.n * s.C_out + co) * s.OH + oh) * s.OW + ow) * 2u : kOOB,
+                               o);
                 }
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
             }
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[b][cb][e] = 0.f;
         }
+        cur = nxt;
+        nxt = next_of(cur);
     }
 }
 
@@ -364,7 +324,7 @@ bool make_geo32(const Shape &s, int TH, int TW, const Config32 &cfg, int num_cu,
     if ((int64_t)g->FR * g->FCP * kRec > kFpBytes32) return false;
     g->ncg = (g->FC - 1 + cfg.vec - 1) / cfg.vec + 1;
     const int tasks = ((g->FR + 1) / 2) * g->ncg * 8;
-    // the next block's window is staged in at most kParts parts of 256 tasks
+    // the next block's window is staged in at most kParts parts of 512 tasks
     if (tasks > kParts * kThreads32) return false;
     g->tiles_h = (s.OH + TH - 1) / TH;
     g->tiles_w = (s.OW + TW - 1) / TW;
@@ -406,6 +366,7 @@ const Config32 &pick32(const Shape &s) { return s.W % 8 == 0 ? kW32v8 : kW32v4; 
 
 bool window32_supports(const Shape &s, int dtype) {
     if (dtype != kDtypeBf16 || s.W % 4 != 0 || s.OW % 4 != 0) return false;
+    if (s.KH != 3 || s.KW != 3 || (s.stride != 1 && s.stride != 2)) return false;
     if ((uint64_t)s.N * s.C_in * s.HW * 2 > kMaxBufferBytes ||
         (uint64_t)s.N * s.C_out * s.OHW * 2 > kMaxBufferBytes)
         return false;
@@ -433,18 +394,20 @@ hipError_t launch_window32(const Shape &s, int epi, const void *x, const void *w
     auto xx = (const uint16_t *)x;
     auto wp = (const uint16_t *)workspace;
     auto yy = (uint16_t *)y;
-#define CBS_W32(C)                                                                                       \
-    if (&cfg == &C) {                                                                                     \
+#define CBS_W32(C, S_)                                                                                   \
+    if (&cfg == &C && s.stride == S_) {                                                                   \
         if (epi == kFused)                                                                                \
-            hipLaunchKernelGGL((window32_bf16<C.mb, C.vec, kFused>), grid, block, 0, st, xx, wp, scale,     \
+            hipLaunchKernelGGL((window32_bf16<C.mb, C.vec, S_, kFused>), grid, block, 0, st, xx, wp, scale, \
                                bias, yy, s, g);                                                          \
         else                                                                                              \
-            hipLaunchKernelGGL((window32_bf16<C.mb, C.vec, kConvOnly>), grid, block, 0, st, xx, wp,        \
+            hipLaunchKernelGGL((window32_bf16<C.mb, C.vec, S_, kConvOnly>), grid, block, 0, st, xx, wp,    \
                                scale, bias, yy, s, g);                                                   \
         return hipGetLastError();                                                                         \
     }
-    CBS_W32(kW32v8)
-    CBS_W32(kW32v4)
+    CBS_W32(kW32v8, 1)
+    CBS_W32(kW32v4, 1)
+    CBS_W32(kW32v8, 2)
+    CBS_W32(kW32v4, 2)
 #undef CBS_W32
     return hipErrorInvalidValue;
 }
