@@ -26,6 +26,7 @@ struct Shape {
 // records and, for stride > 1, columns grouped by residue (CS per group).
 struct WinGeo {
     int TH, TW, FR, FC, CS, FCP;
+    int row_bytes;                     // LDS bytes per window row (32-channel records)
     int ncg;                           // staging column groups per window row
     int tiles_h, tiles_w, co_tiles, n_tiles;
     int n_chunks;                      // 32-channel blocks of C_in

@@ -12,26 +12,29 @@
 // owns pixel blocks wm*MB .. wm*MB+MB-1 (32 pixels each, pixel p of the tile
 // = row p / TW, column p mod TW) and output channels 32*wn .. +31.
 //
-// Reduction order: channel block (32 channels), then the tap (a "unit"),
-// then two 16-channel halves.  LDS holds two window buffers (this channel
-// block and the next) and two weight buffers (this tap and the next); one
-// barrier per unit.  A record holds 32 channels of one input position
-// (window) or one output channel (weights) in 64 bytes, padded to 80: with 5
-// 16-byte slots per record, 16 lanes reading one slot of 16 consecutive
-// records hit 16 distinct bank groups of gfx950's 64-bank LDS, and a
-// fragment -- 8 consecutive channels of one pixel or one output channel per
-// lane -- is one ds_read_b128 whose per-tap part of the address is a
-// uniform offset.
+// Reduction order: channel block (32 channels), then groups of three taps,
+// then the tap, then two 16-channel halves.  LDS holds two window buffers
+// (this channel block and the next) and two weight buffers (this tap group
+// and the next); one barrier per tap group.  A record holds 32 channels of
+// one input position (window) or one output channel (weights) in 64 bytes,
+// padded to 80: with 5 16-byte slots per record, 16 lanes reading one slot of
+// 16 consecutive records hit 16 distinct bank groups of gfx950's 64-bank LDS,
+// and a fragment -- 8 consecutive channels of one pixel or one output
+// channel per lane -- is one ds_read_b128 whose per-tap part of the address
+// is a uniform offset.  The window's row pitch is chosen so that this holds
+// across the row wraps of the tile too.
 //
-// Staging is through registers and runs well ahead of use: a tap's weights
-// (128 channels x 64 bytes, 16 bytes per thread) are requested three units
-// ahead (a ring of three register sets), and the next channel block's whole
-// window (up to 2 parts of 512 tasks, each task 8 channels x VEC columns,
+// Staging is through registers and runs well ahead of use: the next tap
+// group's weights (3 x 16 bytes per thread) are requested at the start of a
+// group and written at its end, and the next channel block's whole window
+// (one or two parts of 512 tasks, each task 8 channels x VEC columns,
 // transposed with byte permutes) is requested at the start of a block and
-// written at its end.  The nine taps are unrolled with the stride fixed at
-// compile time, and blocks advance by counters, so that a unit costs no
-// integer division: the scalar unit, shared by both waves of a SIMD, would
-// otherwise issue more instructions per unit than the matrix core runs.
+// written at its end.  Within a group the fragment reads run a fixed
+// distance ahead of the matrix instructions.  The nine taps are unrolled with
+// the stride fixed at compile time, and blocks advance by counters, so that
+// the loop does no integer division: the scalar unit, shared by both waves
+// of a SIMD, would otherwise issue more instructions per tap than the matrix
+// core runs.
 #include <type_traits>
 
 #include "cbs_device.h"
@@ -46,8 +49,13 @@ constexpr int kBN32 = 128;            // output channels per tile
 constexpr int kCK32 = 32;             // input channels per block
 constexpr int kRec = 80;              // bytes per record (64 data + 16 padding)
 constexpr int kFpBytes32 = 41 * 1024; // one window buffer
-constexpr int kWTB = kBN32 * kRec;    // one weight buffer: one tap x 128 records
-constexpr int kParts = 2;             // window parts (512 tasks each) at most
+constexpr int kWTB = kBN32 * kRec;    // one tap's weights: 128 records
+constexpr int kGT = 3;                // taps per weight group (one barrier each)
+constexpr int kDepth = 4;             // fragment reads in flight ahead of the matrix instructions
+// Window staging parts of 512 tasks: one for 16-byte loads, two for 8-byte
+// loads (narrow images), which is what the register budget of two waves per
+// SIMD allows.
+constexpr int parts_for(int vec) { return vec == 8 ? 1 : 2; }
 
 // Calls f(integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, typename F>
@@ -79,9 +87,10 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wp, const float *__restrict__ scale,
     const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, WinGeo g) {
     __shared__ __attribute__((aligned(16))) unsigned char fps[2][kFpBytes32];
-    __shared__ __attribute__((aligned(16))) unsigned char wbs[2][kWTB];
+    __shared__ __attribute__((aligned(16))) unsigned char wbs[2][kGT * kWTB];
     typedef typename XV32<VEC>::T XT;
     constexpr int kT = 9;  // taps
+    constexpr int kParts = parts_for(VEC);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
@@ -160,7 +169,7 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         const int iw_lo = b.ow0 * S - s.pad;
         const int g0 = iw_lo & ~(VEC - 1);
         const int c0 = g0 + tk_cg[f] * VEC - iw_lo;  // window column of the group's first element (> -VEC)
-        unsigned char *row = fp + (r * g.FCP) * kRec + tk_o[f] * 16;
+        unsigned char *row = fp + r * g.row_bytes + tk_o[f] * 16;
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
             const int c = c0 + j;
@@ -191,10 +200,10 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     for (int b = 0; b < MB; ++b) {
         const int px = (wm * MB + b) * 32 + l32;
         const int i = px / g.TW, j = px - (px / g.TW) * g.TW;
-        abase[b] = (uint32_t)((px < tile_px ? i * S * g.FCP + j : 0) * kRec + hi * 16);
+        abase[b] = (uint32_t)((px < tile_px ? i * S * g.row_bytes + j * kRec : 0) + hi * 16);
     }
     const uint32_t bbase = (uint32_t)((wn * 32 + l32) * kRec + hi * 16);  // weight record of this lane, octet hi
-    const int fcp_b = g.FCP * kRec, cs_b = g.CS * kRec;
+    const int cs_b = g.CS * kRec;
 
     f32x16 acc[MB];
 #pragma unroll
@@ -202,63 +211,74 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
 
-    // Prologue: the window of the first block and the weights of its tap 0
-    // into buffers 0; taps 1 and 2 in flight in ring slots 1 and 2.
+    // Prologue: the window of the first block and the weights of its first
+    // tap group into buffers 0.
     Blk cur = block_at(t_begin, 0, true);
     Blk nxt = next_of(cur);
     XT fpr[kParts][8];
-    u32x4 wreg[3];
-    wreg[0] = w_load(cur, 0);
+    u32x4 wreg[kGT];
+#pragma unroll
+    for (int t = 0; t < kGT; ++t) wreg[t] = w_load(cur, t);
     static_for<0, kParts>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
         fp_load(cur, f, fpr[f]);
     });
-    wreg[1] = w_load(cur, 1);
-    wreg[2] = w_load(cur, 2);
+#pragma unroll
+    for (int t = 0; t < kGT; ++t) *(u32x4 *)(w_dst + t * kWTB) = wreg[t];
     static_for<0, kParts>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
         fp_store(cur, f, fps[0], fpr[f]);
     });
-    *(u32x4 *)w_dst = wreg[0];
     __syncthreads();
 
-    // Unit (block, tap), ring slot tap mod 3, weight buffer (unit index) mod 2
-    // = (step + tap) mod 2 as nine is odd: request the weights three units
-    // ahead; at tap 0 request the next block's window; the two half-steps
-    // (the second's fragments read while the first's MB matrix instructions
-    // run); write the next unit's weights, and after tap 8 the next window;
-    // barrier.
-    bf16x8 fa[2][MB], fb[2];
+    // Group G (three taps; weight buffer G mod 2): request the next group's
+    // weights, and at a block's first group the next block's window; run the
+    // group's 3 x 2 x MB matrix instructions with the fragment reads kDepth
+    // ahead of them (fixed by scheduling fences: left alone, the compiler
+    // sinks each read to just before its use and every instruction waits a
+    // full LDS round trip); write the next group's weights, and after the
+    // last group the next window; barrier.
+    constexpr int kM = kGT * 2 * MB;  // matrix instructions per group
+    bf16x8 fa[kDepth], fb[2];
     for (int step = 0; step < n_steps; ++step) {
         const unsigned char *fp = fps[step & 1];
-        static_for<0, kT>([&](auto tc) {
-            constexpr int tap = decltype(tc)::value;
-            constexpr int sl = tap % 3;
-            wreg[sl] = tap + 3 < kT ? w_load(cur, tap + 3) : w_load(nxt, tap + 3 - kT);
-            if (tap == 0) {
+        static_for<0, kT / kGT>([&](auto gc) {
+            constexpr int gi = decltype(gc)::value;
+            const int wsel = (step * (kT / kGT) + gi) & 1;
+            const unsigned char *wb = &wbs[0][0] + wsel * (kGT * kWTB);
+#pragma unroll
+            for (int t = 0; t < kGT; ++t)
+                wreg[t] = gi + 1 < kT / kGT ? w_load(cur, (gi + 1) * kGT + t) : w_load(nxt, t);
+            if (gi == 0) {
                 static_for<0, kParts>([&](auto fc) {
                     constexpr int f = decltype(fc)::value;
                     fp_load(nxt, f, fpr[f]);
                 });
             }
-            const int wsel = (step + tap) & 1;
-            const unsigned char *wb = &wbs[0][0] + wsel * kWTB;
-            constexpr int kh = tap / 3, kw = tap % 3;
-            const int toff = kh * fcp_b + (kw % S) * cs_b + (kw / S) * kRec;
-            static_for<0, 2>([&](auto hc) {
-                constexpr int h = decltype(hc)::value;
-                fb[h] = *(const bf16x8 *)(wb + bbase + 32 * h);
-#pragma unroll
-                for (int b = 0; b < MB; ++b) fa[h][b] = *(const bf16x8 *)(fp + abase[b] + toff + 32 * h);
+            // fragment m of the group: tap gi*3 + m / (2 MB), half (m / MB) % 2,
+            // pixel block m % MB; its weight fragment is read with its block 0
+            auto issue = [&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                if constexpr (m < kM) {
+                    constexpr int t = m / (2 * MB), h = (m / MB) % 2, b = m % MB;
+                    constexpr int tap = gi * kGT + t, kh = tap / 3, kw = tap % 3;
+                    if constexpr (b == 0) fb[(m / MB) % 2] = *(const bf16x8 *)(wb + t * kWTB + bbase + 32 * h);
+                    const int toff = kh * g.row_bytes + (kw % S) * cs_b + (kw / S) * kRec;
+                    fa[m % kDepth] = *(const bf16x8 *)(fp + abase[b] + toff + 32 * h);
+                }
+            };
+            static_for<0, kDepth>([&](auto mc) { issue(mc); });
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, kM>([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                constexpr int b = m % MB;
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m % kDepth], fb[(m / MB) % 2], acc[b], 0, 0, 0);
+                issue(std::integral_constant<int, m + kDepth>{});
+                __builtin_amdgcn_sched_barrier(0);
             });
-            static_for<0, 2>([&](auto hc) {
-                constexpr int h = decltype(hc)::value;
 #pragma unroll
-                for (int b = 0; b < MB; ++b)
-                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[h][b], fb[h], acc[b], 0, 0, 0);
-            });
-            *(u32x4 *)(w_dst + (wsel ^ 1) * kWTB) = wreg[(sl + 1) % 3];
-            if (tap == kT - 1) {
+            for (int t = 0; t < kGT; ++t) *(u32x4 *)(w_dst + (wsel ^ 1) * (kGT * kWTB) + t * kWTB) = wreg[t];
+            if (gi == kT / kGT - 1) {
                 static_for<0, kParts>([&](auto fc) {
                     constexpr int f = decltype(fc)::value;
                     fp_store(nxt, f, fps[(step + 1) & 1], fpr[f]);
@@ -320,12 +340,21 @@ bool make_geo32(const Shape &s, int TH, int TW, const Config32 &cfg, int num_cu,
     g->FC = (TW - 1) * s.stride + s.KW;
     g->CS = (g->FC + s.stride - 1) / s.stride;
     g->FCP = s.stride * g->CS;
-    if (g->FCP % 2 == 0) g->FCP += 1;
-    if ((int64_t)g->FR * g->FCP * kRec > kFpBytes32) return false;
+    // Row pitch: at least the row's records, and congruent to TW * 80 / S
+    // modulo 256 / S bytes, so that output pixel (i, j) of the tile reads a
+    // record whose 16-byte bank group is 5 (i TW + j) + (a per-tap constant)
+    // mod 16: the 16 consecutive pixels of a half-wave's fragment read hit 16
+    // distinct groups of four banks even where they wrap onto the next row.
+    const int mod = 256 / s.stride;
+    const int want = (TW * kRec / s.stride) % mod;
+    int rb = g->FCP * kRec;
+    rb += ((want - rb % mod) % mod + mod) % mod;
+    g->row_bytes = rb;
+    if ((int64_t)g->FR * g->row_bytes > kFpBytes32) return false;
     g->ncg = (g->FC - 1 + cfg.vec - 1) / cfg.vec + 1;
     const int tasks = ((g->FR + 1) / 2) * g->ncg * 8;
-    // the next block's window is staged in at most kParts parts of 512 tasks
-    if (tasks > kParts * kThreads32) return false;
+    // the next block's window is staged in at most parts_for(vec) parts of 512 tasks
+    if (tasks > parts_for(cfg.vec) * kThreads32) return false;
     g->tiles_h = (s.OH + TH - 1) / TH;
     g->tiles_w = (s.OW + TW - 1) / TW;
     g->co_tiles = (s.C_out + kBN32 - 1) / kBN32;
