@@ -66,8 +66,10 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
+// Half h of lo_word in the low half, half h of hi_word in the high half (one
+// byte permute).
 __device__ __forceinline__ uint32_t pair16(uint32_t lo_word, uint32_t hi_word, int h) {
-    return h == 0 ? ((lo_word & 0xFFFFu) | (hi_word << 16)) : ((lo_word >> 16) | (hi_word & 0xFFFF0000u));
+    return __builtin_amdgcn_perm(hi_word, lo_word, h == 0 ? 0x05040100u : 0x07060302u);
 }
 
 template <int VEC> struct XV32;
@@ -88,6 +90,7 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, WinGeo g) {
     __shared__ __attribute__((aligned(16))) unsigned char fps[2][kFpBytes32];
     __shared__ __attribute__((aligned(16))) unsigned char wbs[2][kGT * kWTB];
+    __shared__ __attribute__((aligned(16))) unsigned char sink[64 * 16];  // target of masked-off stores
     typedef typename XV32<VEC>::T XT;
     constexpr int kT = 9;  // taps
     constexpr int kParts = parts_for(VEC);
@@ -96,7 +99,14 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     const int wm = wave >> 2, wn = wave & 3;
     const int l32 = lane & 31, hi = lane >> 5;
 
-    const int t_begin = (int)blockIdx.x * g.tiles_per_wg;
+    // XCD-aware placement: the XCDs take workgroups round-robin (XCD =
+    // block id mod 8); rank the workgroups so that each XCD runs one
+    // contiguous range of tiles, which puts the 128-channel tiles of one
+    // image (consecutive tile indices) on one XCD, where they share its L2
+    // for the input window instead of each fetching it from memory.
+    const int xcd = (int)blockIdx.x & 7, q8 = g.n_wg >> 3, r8 = g.n_wg & 7;
+    const int rank = xcd * q8 + min(xcd, r8) + ((int)blockIdx.x >> 3);
+    const int t_begin = rank * g.tiles_per_wg;
     const int t_end = min(t_begin + g.tiles_per_wg, g.n_tiles);
     if (t_begin >= t_end) return;  // uniform
     const int n_steps = (t_end - t_begin) * g.n_chunks;  // (tile, channel block) pairs
@@ -149,7 +159,15 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         tk_r[f] = 2 * (rest / g.ncg) + ((t >> 2) & 1);
         if (f >= nparts) tk_r[f] = g.FR;  // no rows: idle task
     }
-    auto fp_load = [&](const Blk &b, int f, XT (&reg)[8]) {
+    // A task's 8 loads (channel c of its octet) are issued one at a time so
+    // that they can be spread between matrix instructions: fp_off gives the
+    // task's first byte offset and the number of its channels to load (0 if
+    // none).
+    struct LdPlan {
+        uint32_t off0;
+        int nch;
+    };
+    auto fp_plan = [&](const Blk &b, int f) {
         const int iw_lo = b.ow0 * S - s.pad;
         const int g0 = iw_lo & ~(VEC - 1);  // floor to a multiple of VEC
         const int r = tk_r[f];
@@ -158,30 +176,44 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         const bool ok = b.live && r < g.FR && (unsigned)ih < (unsigned)s.H && iw0 >= 0 && iw0 < s.W &&
                         iw0 + VEC - 1 >= iw_lo && iw0 <= iw_lo + g.FC - 1;
         const int ci0 = b.ck * kCK32 + 8 * tk_o[f];
-        const uint32_t off0 = (uint32_t)(((b.n * s.C_in + ci0) * s.H + ih) * s.W + iw0) * 2u;
+        LdPlan pl;
+        pl.off0 = (uint32_t)(((b.n * s.C_in + ci0) * s.H + ih) * s.W + iw0) * 2u;
+        pl.nch = ok ? min(8, s.C_in - ci0) : 0;
+        return pl;
+    };
+    auto fp_load_one = [&](const LdPlan &pl, int c) {
+        return XV32<VEC>::load(xr, c < pl.nch ? pl.off0 + (uint32_t)(c * s.HW) * 2u : kOOB);
+    };
+    auto fp_load = [&](const Blk &b, int f, XT (&reg)[8]) {
+        const LdPlan pl = fp_plan(b, f);
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-            reg[c] = XV32<VEC>::load(xr, (ok && ci0 + c < s.C_in) ? off0 + (uint32_t)(c * s.HW) * 2u : kOOB);
+        for (int c = 0; c < 8; ++c) reg[c] = fp_load_one(pl, c);
+    };
+    // Column j of a task is stored on its own, so that the stores can be
+    // spread between matrix instructions; a column outside the window (or
+    // of an idle task) goes to this lane's slot of the sink instead of
+    // branching.  c0: window column of the task's first element (> -VEC).
+    auto fp_c0 = [&](const Blk &b, int f) {
+        const int iw_lo = b.ow0 * S - s.pad;
+        return (iw_lo & ~(VEC - 1)) + tk_cg[f] * VEC - iw_lo;
+    };
+    unsigned char *const sink_lane = sink + lane * 16;
+    auto fp_store_col = [&](int c0, int f, int j, unsigned char *fp, const XT (&reg)[8]) {
+        const int r = tk_r[f];
+        const int c = c0 + j;
+        // window column c sits at (c mod S) * CS + c / S: the columns of one
+        // phase are contiguous, so a tap's columns are consecutive
+        const int pos = S == 1 ? c : (c & 1) * g.CS + (c >> 1);
+        const bool ok = r < g.FR && c >= 0 && c < g.FC;
+        u32x4 v;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) v[d] = pair16(reg[2 * d][j >> 1], reg[2 * d + 1][j >> 1], j & 1);
+        *(u32x4 *)(ok ? fp + r * g.row_bytes + tk_o[f] * 16 + pos * kRec : sink_lane) = v;
     };
     auto fp_store = [&](const Blk &b, int f, unsigned char *fp, const XT (&reg)[8]) {
-        const int r = tk_r[f];
-        if (r >= g.FR) return;
-        const int iw_lo = b.ow0 * S - s.pad;
-        const int g0 = iw_lo & ~(VEC - 1);
-        const int c0 = g0 + tk_cg[f] * VEC - iw_lo;  // window column of the group's first element (> -VEC)
-        unsigned char *row = fp + r * g.row_bytes + tk_o[f] * 16;
+        const int c0 = fp_c0(b, f);
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-            const int c = c0 + j;
-            if (c < 0 || c >= g.FC) continue;
-            // window column c sits at (c mod S) * CS + c / S: the columns of
-            // one phase are contiguous, so a tap's columns are consecutive
-            const int pos = S == 1 ? c : (c & 1) * g.CS + (c >> 1);
-            u32x4 v;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) v[d] = pair16(reg[2 * d][j >> 1], reg[2 * d + 1][j >> 1], j & 1);
-            *(u32x4 *)(row + pos * kRec) = v;
-        }
+        for (int j = 0; j < VEC; ++j) fp_store_col(c0, f, j, fp, reg);
     };
 
     // ---- weight staging: one tap x 128 channels x 4 octets; thread: channel
@@ -232,29 +264,39 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     __syncthreads();
 
     // Group G (three taps; weight buffer G mod 2): request the next group's
-    // weights, and at a block's first group the next block's window; run the
-    // group's 3 x 2 x MB matrix instructions with the fragment reads kDepth
-    // ahead of them (fixed by scheduling fences: left alone, the compiler
-    // sinks each read to just before its use and every instruction waits a
-    // full LDS round trip); write the next group's weights, and after the
-    // last group the next window; barrier.
-    constexpr int kM = kGT * 2 * MB;  // matrix instructions per group
+    // weights; run the group's 3 x 2 x MB matrix instructions with the
+    // fragment reads kDepth ahead of them, and between them write the next
+    // group's weights, in a block's first group load the next window, and in
+    // its last group write it; barrier.  The order is fixed by scheduling
+    // fences: left alone, the compiler sinks each read to just before its
+    // use, so that every instruction waits a full LDS round trip, and bunches
+    // the loads and stores, which stalls issue.
+    constexpr int kM = kGT * 2 * MB;     // matrix instructions per group
+    constexpr int kCols = kParts * VEC;  // window columns each thread stores per block
+    static_assert(kCols * 5 <= kM && 40 < kM && kParts * 16 <= kM, "staging slots exceed the group");
     bf16x8 fa[kDepth], fb[2];
     for (int step = 0; step < n_steps; ++step) {
         const unsigned char *fp = fps[step & 1];
         static_for<0, kT / kGT>([&](auto gc) {
             constexpr int gi = decltype(gc)::value;
+            constexpr bool last_group = gi == kT / kGT - 1;
             const int wsel = (step * (kT / kGT) + gi) & 1;
             const unsigned char *wb = &wbs[0][0] + wsel * (kGT * kWTB);
+            unsigned char *const w_next = w_dst + (wsel ^ 1) * (kGT * kWTB);
 #pragma unroll
             for (int t = 0; t < kGT; ++t)
                 wreg[t] = gi + 1 < kT / kGT ? w_load(cur, (gi + 1) * kGT + t) : w_load(nxt, t);
+            LdPlan lps[kParts];
             if (gi == 0) {
-                static_for<0, kParts>([&](auto fc) {
-                    constexpr int f = decltype(fc)::value;
-                    fp_load(nxt, f, fpr[f]);
-                });
+#pragma unroll
+                for (int f = 0; f < kParts; ++f) lps[f] = fp_plan(nxt, f);
             }
+            int c0s[kParts];
+            if (last_group) {
+#pragma unroll
+                for (int f = 0; f < kParts; ++f) c0s[f] = fp_c0(nxt, f);
+            }
+            unsigned char *const fp_next = fps[(step + 1) & 1];
             // fragment m of the group: tap gi*3 + m / (2 MB), half (m / MB) % 2,
             // pixel block m % MB; its weight fragment is read with its block 0
             auto issue = [&](auto mc) {
@@ -274,16 +316,22 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
                 constexpr int b = m % MB;
                 acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m % kDepth], fb[(m / MB) % 2], acc[b], 0, 0, 0);
                 issue(std::integral_constant<int, m + kDepth>{});
+                // next block's window: load q (channel q mod 8 of part q / 8)
+                // after matrix instruction 2q + 1 of the first group
+                if constexpr (gi == 0 && m % 2 == 1 && m / 2 < kParts * 8) {
+                    constexpr int q = m / 2;
+                    fpr[q / 8][q % 8] = fp_load_one(lps[q / 8], q % 8);
+                }
+                // next window: column q after matrix instruction 5q + 1
+                if constexpr (last_group && m % 5 == 1 && m / 5 < kCols) {
+                    constexpr int q = m / 5;
+                    fp_store_col(c0s[q / VEC], q / VEC, q % VEC, fp_next, fpr[q / VEC]);
+                }
+                // next group's weights: tap t after matrix instruction 20 + 10 t
+                if constexpr (m >= 20 && m % 10 == 0 && (m - 20) / 10 < kGT)
+                    *(u32x4 *)(w_next + ((m - 20) / 10) * kWTB) = wreg[(m - 20) / 10];
                 __builtin_amdgcn_sched_barrier(0);
             });
-#pragma unroll
-            for (int t = 0; t < kGT; ++t) *(u32x4 *)(w_dst + (wsel ^ 1) * (kGT * kWTB) + t * kWTB) = wreg[t];
-            if (gi == kT / kGT - 1) {
-                static_for<0, kParts>([&](auto fc) {
-                    constexpr int f = decltype(fc)::value;
-                    fp_store(nxt, f, fps[(step + 1) & 1], fpr[f]);
-                });
-            }
             __syncthreads();
         });
 
