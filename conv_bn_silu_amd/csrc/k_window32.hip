@@ -275,6 +275,13 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     constexpr int kCols = kParts * VEC;  // window columns each thread stores per block
     static_assert(kCols * 5 <= kM && 40 < kM && kParts * 16 <= kM, "staging slots exceed the group");
     bf16x8 fa[kDepth], fb[2];
+    // BN factors of this lane's output channel, loaded a tile ahead
+    float sc_next, bi_next;
+    {
+        const int co = cur.co0 + wn * 32 + l32;
+        sc_next = co < s.C_out ? scale[co] : 0.f;
+        bi_next = co < s.C_out ? bias[co] : 0.f;
+    }
     for (int step = 0; step < n_steps; ++step) {
         const unsigned char *fp = fps[step & 1];
         static_for<0, kT / kGT>([&](auto gc) {
@@ -337,20 +344,28 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
 
         if (cur.ck == g.n_chunks - 1) {
             // ---- epilogue for the finished tile ----------------------------
-            // (The tile width is passed through an empty asm so that the pixel
-            // coordinates below are computed here, not hoisted out of the loop
-            // into registers the reduction needs.)
+            // Row i = px / TW as (px * ceil(2^20 / TW)) >> 20, exact for the
+            // tile's pixels (px < 2 * MB * 32 <= 448, TW <= 448); a division
+            // would cost dozens of instructions per store.  (The tile width
+            // and its reciprocal pass through an empty asm so that the pixel
+            // coordinates are computed here, not hoisted out of the loop into
+            // registers the reduction needs.)
             int tw_e = g.TW;
-            asm volatile("" : "+s"(tw_e));
+            uint32_t rcp_tw = ((1u << 20) + (uint32_t)g.TW - 1) / (uint32_t)g.TW;
+            asm volatile("" : "+s"(tw_e), "+s"(rcp_tw));
             const int co = cur.co0 + wn * 32 + l32;
-            const float sc = co < s.C_out ? scale[co] : 0.f;
-            const float bi = co < s.C_out ? bias[co] : 0.f;
+            const float sc = sc_next, bi = bi_next;
+            if (cur.tile + 1 < t_end) {  // the next tile's factors, ahead of its epilogue
+                const int co_n = nxt.co0 + wn * 32 + l32;
+                sc_next = co_n < s.C_out ? scale[co_n] : 0.f;
+                bi_next = co_n < s.C_out ? bias[co_n] : 0.f;
+            }
 #pragma unroll
             for (int b = 0; b < MB; ++b) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int px = (wm * MB + b) * 32 + 8 * q + 4 * hi;
-                    const int i = px / tw_e, j = px - i * tw_e;
+                    const int i = (int)(((uint32_t)px * rcp_tw) >> 20), j = px - i * tw_e;
                     const int oh = cur.oh0 + i, ow = cur.ow0 + j;
                     const bool ok = px < tile_px && oh < s.OH && ow < s.OW && co < s.C_out;
                     u32x2 o;
