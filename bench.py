@@ -110,6 +110,7 @@ def time_steps(step, steps: int, warmup: int, stream) -> dict:
     t0 = time.perf_counter()
     for i in range(steps):
         step(i)
+    issued = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -125,7 +126,8 @@ def time_steps(step, steps: int, warmup: int, stream) -> dict:
         step(i)
     r1.record(stream)
     torch.cuda.synchronize()
-    return {"wall_s": wall, "launch_mean_s": sum(durs) / len(durs), "launch_median_s": durs[len(durs) // 2],
+    return {"wall_s": wall, "host_issue_s": issued, "launch_mean_s": sum(durs) / len(durs),
+            "launch_median_s": durs[len(durs) // 2],
             "launch_min_s": durs[0], "region_per_step_s": r0.elapsed_time(r1) * 1e-3 / steps}
 
 
@@ -141,10 +143,17 @@ def measure_fused(key: str, steps: int, warmup: int, variant: str = "auto", laye
     stream = torch.cuda.current_stream(torch.device("cuda", 0))
     sp = stream.cuda_stream
 
+    # Arguments bound once per buffer set, and the C entry point called
+    # directly: at tens of microseconds per launch the Python side must stay
+    # well ahead of the GPU, or the timing measures the host.
+    fn, handle = B.lib.conv_bn_silu_run_variant, lib.handle
+    args = [(handle, v, L.xs[j].data_ptr(), L.w.data_ptr(), L.sc.data_ptr(), L.bi.data_ptr(),
+             L.ys[j][0].data_ptr(), *L.geo, sp) for j in range(L.sets)]
+
     def step(i):
-        j = i % L.sets
-        lib.run_ptr(v, L.xs[j].data_ptr(), L.w.data_ptr(), L.sc.data_ptr(), L.bi.data_ptr(),
-                    L.ys[j][0].data_ptr(), *L.geo, sp)
+        rc = fn(*args[i % L.sets])
+        if rc:
+            lib.run_ptr(*args[i % L.sets][1:])  # raises with the status and HIP error
 
     t = time_steps(step, steps, warmup, stream)
     # Average launch duration: HIP events around the whole back-to-back
@@ -154,7 +163,8 @@ def measure_fused(key: str, steps: int, warmup: int, variant: str = "auto", laye
     kern = t["region_per_step_s"]
     return {"key": key, "wl": wl, "variant": B.variant_name(v), "sets": L.sets,
             "ms_per_step": t["wall_s"] / steps * 1e3, "tflops": wl.flops / (t["wall_s"] / steps) / 1e12,
-            "kernel_us_mean": kern * 1e6, "launch_events_us_mean": t["launch_mean_s"] * 1e6,
+            "kernel_us_mean": kern * 1e6, "host_issue_us_per_step": t["host_issue_s"] / steps * 1e6,
+            "launch_events_us_mean": t["launch_mean_s"] * 1e6,
             "launch_events_us_median": t["launch_median_s"] * 1e6,
             "kernel_us_min": t["launch_min_s"] * 1e6, "region_us_per_step": t["region_per_step_s"] * 1e6,
             "roofline": roofline(wl, kern), "hbm_gbs_alg": wl.algorithmic_bytes / kern / 1e9,
@@ -170,11 +180,15 @@ def measure_unfused(key: str, steps: int, warmup: int) -> dict:
     stream = torch.cuda.current_stream(torch.device("cuda", 0))
     sp = stream.cuda_stream
 
+    fn, handle = B.lib.conv_bn_silu_run_unfused, lib.handle
+    args = [(handle, L.xs[j].data_ptr(), L.w.data_ptr(), L.sc.data_ptr(), L.bi.data_ptr(),
+             L.ys[j][1].data_ptr(), L.ys[j][2].data_ptr(), L.ys[j][0].data_ptr(), *L.geo, sp)
+            for j in range(L.sets)]
+
     def step(i):
-        j = i % L.sets
-        y, t1, t2 = L.ys[j]
-        lib.run_unfused_ptr(L.xs[j].data_ptr(), L.w.data_ptr(), L.sc.data_ptr(), L.bi.data_ptr(),
-                            t1.data_ptr(), t2.data_ptr(), y.data_ptr(), *L.geo, sp)
+        rc = fn(*args[i % L.sets])
+        if rc:
+            lib.run_unfused_ptr(*args[i % L.sets][1:])  # raises with the status and HIP error
 
     t = time_steps(step, steps, warmup, stream)
     return {"us_per_step": t["region_per_step_s"] * 1e6, "wall_us_per_step": t["wall_s"] / steps * 1e6}
@@ -276,6 +290,7 @@ def main():
         "config": {"workload": wl.name, "N": wl.N, "C_in": wl.C_in, "H": wl.H, "W": wl.W, "C_out": wl.C_out,
                    "KH": wl.KH, "KW": wl.KW, "stride": wl.stride, "pad": wl.pad, "variant": r["variant"],
                    "rotated_buffer_sets": r["sets"], "kernel_us_mean": round(r["kernel_us_mean"], 3),
+                   "host_issue_us_per_step": round(r["host_issue_us_per_step"], 3),
                    "launch_events_us_mean": round(r["launch_events_us_mean"], 3),
                    "launch_events_us_median": round(r["launch_events_us_median"], 3),
                    "algorithmic_bytes": wl.algorithmic_bytes, "flops": wl.flops},
