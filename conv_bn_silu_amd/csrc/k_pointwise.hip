@@ -1,6 +1,3 @@
-#ifndef PWPD
-#define PWPD 2
-#endif
 // k_pointwise.hip -- the 1x1 (stride 1, no padding) layer as a streaming GEMM.
 //
 // For a 1x1 convolution the implicit GEMM has no window: row m of the pixel
@@ -62,6 +59,7 @@ constexpr int kBK = 32;                 // input channels per block
 constexpr int kPieces = kBK * kMaxL / 8;  // 16-byte pieces of a block at most
 constexpr int kTPT = (kPieces + kThreadsPw - 1) / kThreadsPw;  // pieces per thread
 constexpr int kDepth = 4;               // fragment reads ahead of the MFMAs
+constexpr int kPD = 2;                  // channel blocks in flight in registers
 constexpr int kEpiPitch = 2 * kMaxL + 16;  // output staging: bytes per channel row (464)
 constexpr int kEpiBytes = kWaves * 32 * kEpiPitch;
 
@@ -279,7 +277,7 @@ hipError_t launch_pw(const Shape &s, const void *x, const void *w, const float *
     const int L = range_len(s, num_cu);
     const int n_ranges = (s.M + L - 1) / L;
     const int items = n_ranges * co_tiles;
-    hipLaunchKernelGGL((pointwise_bf16<KS, PWPD, EPI>), dim3(items), dim3(kThreadsPw), 0, st, (const uint16_t *)x,
+    hipLaunchKernelGGL((pointwise_bf16<KS, kPD, EPI>), dim3(items), dim3(kThreadsPw), 0, st, (const uint16_t *)x,
                        (const uint16_t *)w, scale, bias, (uint16_t *)y, s, L, n_ranges, co_tiles);
     return hipGetLastError();
 }
