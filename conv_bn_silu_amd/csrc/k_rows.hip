@@ -23,9 +23,15 @@
 //  * A unit is (output row, 16-channel chunk): its 48 input row segments
 //    are loaded two units ahead into registers (16-byte loads of 8 columns,
 //    split into even and odd columns with byte permutes; the shifted odd
-//    array takes its first element from the left neighbour lane), written
-//    to one of three LDS sets one unit ahead, and read by the unit after a
-//    barrier.
+//    array takes its first element, the column left of the segment, from a
+//    4-byte load of the two columns before it), written to one of three LDS
+//    sets one unit ahead, and read by the unit after a barrier.
+//  * The loop body is one output row (all its chunks, unrolled; two rows
+//    when the chunk count is odd, so that the register slots of the units
+//    repeat), with the epilogue at a fixed place in it: every iteration
+//    issues the same memory operations in the same order, so the waits
+//    for each unit's data count exactly the operations issued since and
+//    never drain the loads in flight for the units ahead.
 //  * The unit's weights (32 channels x 144 k per wave, 9 fragments of 16
 //    bytes per lane) are loaded one unit ahead into registers.
 //  * Row pitch in LDS: 2*OW bytes, an odd multiple of 64 for OW = 32*NB
@@ -74,7 +80,8 @@ struct RowsGeo {
     static constexpr int MAXT = (TASKS + kRowsThreads - 1) / kRowsThreads;
 };
 
-template <int NB, int EPI>
+// NCH: 16-channel chunks of C_in (C_in = 16 * NCH).
+template <int NB, int NCH, int EPI>
 __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ scale,
     const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int co_tiles, int ranks_per_xcd,
@@ -94,8 +101,11 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     const int rows_total = s.N * s.OH;
     if (j >= rows_total) return;  // uniform
     const int steps = (rows_total - j + n_ranks - 1) / n_ranks;  // output rows of this rank
-    const int nchunks = s.C_in / kChunk;
-    const int units = steps * nchunks;
+    constexpr int nchunks = NCH;
+    constexpr int RPI = NCH % 2 == 0 ? 1 : 2;  // output rows per loop iteration
+    constexpr int UPI = RPI * NCH;              // units per iteration (even)
+    const int iters = (steps + RPI - 1) / RPI;
+    const int units = steps * nchunks;  // units past this one (a padding row) load zeros and store nothing
     const int segs = s.W / 8;
     const int tasks = 3 * kChunk * segs;
 
@@ -120,7 +130,6 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
         tk_goff[q] = (uint32_t)((ci * s.H + kh) * s.W + 8 * seg) * 2u;
         tk_lds[q] = (ci * 9 + kh * 3) * G::P + 8 * seg;
     }
-    const int prev_lane_addr = 4 * ((lane + 63) & 63);
 
     struct UnitPos {
         int n, oh, chunk;
@@ -145,7 +154,8 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
             const bool ok = live && tk_valid[q] && (uint32_t)ih < (uint32_t)s.H;
             const uint32_t off = base + tk_goff[q];
             a[q] = buf_load16(xr, ok ? off : kOOB);
-            pv[q] = buf_load4(xr, ok && lane == 0 && !tk_first[q] ? off - 4u : kOOB);
+            // columns 8 seg - 2, 8 seg - 1 (none left of the row: zero padding)
+            pv[q] = buf_load4(xr, ok && !tk_first[q] ? off - 4u : kOOB);
         }
     };
     // Split 8 input columns into the unit's three tap arrays (4 output
@@ -158,9 +168,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
             const uint32_t e1 = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
             const uint32_t o0 = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
             const uint32_t o1 = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
-            uint32_t prev = (uint32_t)__builtin_amdgcn_ds_bpermute(prev_lane_addr, (int)o1);
-            prev = lane == 0 ? pv[q] : prev;
-            prev = tk_first[q] ? 0u : prev;
+            const uint32_t prev = pv[q];  // high half: column 8 seg - 1
             if (!tk_valid[q]) continue;
             unsigned char *dst = set + tk_lds[q];
             *(u32x2 *)(dst) = u32x2{__builtin_amdgcn_perm(o0, prev, 0x05040302u), __builtin_amdgcn_alignbit(o1, o0, 16)};
@@ -243,12 +251,14 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
                 acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][b], __builtin_bit_cast(bf16x8, wcurf[ks]),
                                                                  acc[b], 0, 0, 0);
         });
-        const UnitPos up = unit_pos(u);
-        if (up.chunk != nchunks - 1) return;  // uniform
-        // Epilogue of output row (n, oh): lane holds channel co_lane, pixels
-        // 32b + 8*(i>>2) + 4*(lane>>5) + (i&3).
+    };
+    // Epilogue of the rank's output row t (stores dropped for a padding row
+    // t >= steps): lane holds channel co_lane, pixels
+    // 32b + 8*(i>>2) + 4*(lane>>5) + (i&3).
+    auto epilogue = [&](int t) {
+        const UnitPos up = unit_pos(t * nchunks);
         const uint32_t obase = (uint32_t)(((up.n * s.C_out + co_lane) * s.OH + up.oh) * s.OW) * 2u;
-        const bool cok = co_lane < s.C_out;
+        const bool cok = co_lane < s.C_out && t < steps;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
 #pragma unroll
@@ -266,13 +276,16 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
         }
     };
     static_assert(kRowsPD == 2, "register slots alternate with unit parity");
-    for (int u0 = 0; u0 < units; u0 += 2) {
-        run_unit(u0, std::integral_constant<int, 1>{});
-        if (u0 + 1 < units) run_unit(u0 + 1, std::integral_constant<int, 0>{});
+    for (int it = 0; it < iters; ++it) {
+        rows_for<0, UPI>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            run_unit(it * UPI + c, std::integral_constant<int, (c + 1) % 2>{});
+            if constexpr (c % NCH == NCH - 1) epilogue(it * RPI + c / NCH);
+        });
     }
 }
 
-template <int NB, int EPI>
+template <int NB, int NCH, int EPI>
 hipError_t launch_rows_t(const Shape &s, const void *x, const void *w, const float *scale, const float *bias,
                          void *y, hipStream_t st, int num_cu) {
     const int co_tiles = (s.C_out + kRowsTile - 1) / kRowsTile;
@@ -280,7 +293,7 @@ hipError_t launch_rows_t(const Shape &s, const void *x, const void *w, const flo
     int n_ranks = (num_cu + co_tiles - 1) / co_tiles;
     if (n_ranks > rows_total) n_ranks = rows_total;
     const int ranks_per_xcd = (n_ranks + 7) / 8;
-    hipLaunchKernelGGL((rows_bf16<NB, EPI>), dim3(ranks_per_xcd * 8 * co_tiles), dim3(kRowsThreads), 0, st,
+    hipLaunchKernelGGL((rows_bf16<NB, NCH, EPI>), dim3(ranks_per_xcd * 8 * co_tiles), dim3(kRowsThreads), 0, st,
                        (const uint16_t *)x, (const uint16_t *)w, scale, bias, (uint16_t *)y, s, co_tiles,
                        ranks_per_xcd, n_ranks);
     return hipGetLastError();
@@ -301,12 +314,18 @@ bool rows_pointers_ok(const void *x, const void *w, const void *y) {
 
 hipError_t launch_rows(const Shape &s, int epi, const void *x, const void *w, const float *scale, const float *bias,
                        void *y, hipStream_t st, int num_cu) {
-#define CBS_ROWS(NB_)                                                                                 \
-    if (s.OW <= RowsGeo<NB_>::OWMAX)                                                                  \
-        return epi == kFused ? launch_rows_t<NB_, kFused>(s, x, w, scale, bias, y, st, num_cu)        \
-                             : launch_rows_t<NB_, kConvOnly>(s, x, w, scale, bias, y, st, num_cu);
+#define CBS_ROWS2(NB_, NCH_)                                                                           \
+    if (s.C_in == kChunk * NCH_)                                                                       \
+        return epi == kFused ? launch_rows_t<NB_, NCH_, kFused>(s, x, w, scale, bias, y, st, num_cu)   \
+                             : launch_rows_t<NB_, NCH_, kConvOnly>(s, x, w, scale, bias, y, st, num_cu);
+#define CBS_ROWS(NB_)                                                                                  \
+    if (s.OW <= RowsGeo<NB_>::OWMAX) {                                                                 \
+        CBS_ROWS2(NB_, 1) CBS_ROWS2(NB_, 2) CBS_ROWS2(NB_, 3) CBS_ROWS2(NB_, 4)                        \
+        return hipErrorInvalidValue;                                                                   \
+    }
     CBS_ROWS(1) CBS_ROWS(3) CBS_ROWS(5)
 #undef CBS_ROWS
+#undef CBS_ROWS2
     return hipErrorInvalidValue;
 }
 

@@ -84,6 +84,10 @@ SWEEP = [
     (1, 64, 33, 64, 128, 3, 3, 2, 1),
     (3, 32, 20, 320, 136, 3, 3, 2, 1),
     (2, 48, 12, 96, 64, 3, 3, 2, 1),
+    # more output rows than ranks with an odd chunk count: several loop
+    # iterations of two rows each, and a padding row at the end for some ranks
+    (6, 48, 200, 32, 64, 3, 3, 2, 1),
+    (5, 16, 240, 16, 24, 3, 3, 2, 1),
 ]
 
 
