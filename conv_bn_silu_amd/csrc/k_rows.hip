@@ -22,10 +22,12 @@
 //    contiguous window of x and y, which keeps DRAM pages open.
 //  * A unit is (output row, 16-channel chunk): its 48 input row segments
 //    are loaded two units ahead into registers (16-byte loads of 8 columns,
-//    split into even and odd columns with byte permutes; the shifted odd
-//    array takes its first element, the column left of the segment, from a
-//    4-byte load of the two columns before it), written to one of three LDS
-//    sets one unit ahead, and read by the unit after a barrier.
+//    split into even and odd columns with byte permutes), written to one of
+//    three LDS sets one unit ahead, and read by the unit after a barrier.
+//    The shifted odd array needs the column left of each segment: a wave's
+//    load covers 63 consecutive segments in lanes 1..63 and repeats the one
+//    before them in lane 0, so every lane takes that column from the lane
+//    below it by a DPP wave shift (lane 0 only supplies it).
 //  * The loop body is one output row (all its chunks, unrolled; two rows
 //    when the chunk count is odd, so that the register slots of the units
 //    repeat), with the epilogue at a fixed place in it: every iteration
@@ -75,9 +77,10 @@ struct RowsGeo {
     static constexpr int OWMAX = 32 * NB;
     static constexpr int P = (NB % 2 == 1) ? 2 * OWMAX : 2 * OWMAX + 64;  // row pitch, odd multiple of 64
     static constexpr int SET = kKRows * P;                                // bytes per set
-    // 16-byte tasks per unit: 3 input rows x 16 channels x (2*OWMAX)/8 segments
+    // 16-byte tasks per unit: 3 input rows x 16 channels x (2*OWMAX)/8
+    // segments, 63 new ones per wave-wide load
     static constexpr int TASKS = 3 * kChunk * (2 * OWMAX / 8);
-    static constexpr int MAXT = (TASKS + kRowsThreads - 1) / kRowsThreads;
+    static constexpr int MAXT = ((TASKS + 62) / 63 + kRowsWaves - 1) / kRowsWaves;
 };
 
 // NCH: 16-channel chunks of C_in (C_in = 16 * NCH).
@@ -113,18 +116,21 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)s.C_out * s.K * 2u);
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)s.N * s.C_out * s.OHW * 2u);
 
-    // Copy task q of this thread (index tid + q*threads): input row kh of the
-    // unit, channel ci of the chunk, 8-column segment seg.  Consecutive lanes
-    // hold consecutive segments of one row unless seg == 0.
+    // Copy task q of this thread: segment t = 63 (4 q + wave) + lane - 1 of
+    // the unit, i.e. input row kh of the unit, channel ci of the chunk,
+    // 8-column segment seg.  Consecutive lanes hold consecutive segments;
+    // lane 0 holds the segment before lane 1's and is only loaded.
     int tk_kh[G::MAXT], tk_lds[G::MAXT];
     uint32_t tk_goff[G::MAXT];
-    bool tk_valid[G::MAXT], tk_first[G::MAXT];
+    bool tk_load[G::MAXT], tk_valid[G::MAXT], tk_first[G::MAXT];
 #pragma unroll
     for (int q = 0; q < G::MAXT; ++q) {
-        const int t = tid + q * kRowsThreads;
+        const int traw = 63 * (q * kRowsWaves + wave) + lane - 1;
+        const int t = traw < 0 ? 0 : traw;
         const int kh = t / (kChunk * segs), rem = t - kh * (kChunk * segs);
         const int ci = rem / segs, seg = rem - ci * segs;
-        tk_valid[q] = t < tasks;
+        tk_load[q] = traw >= 0 && t < tasks;
+        tk_valid[q] = lane > 0 && t < tasks;
         tk_first[q] = seg == 0;
         tk_kh[q] = kh;
         tk_goff[q] = (uint32_t)((ci * s.H + kh) * s.W + 8 * seg) * 2u;
@@ -142,8 +148,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     };
 
     u32x4 ra[kRowsPD][G::MAXT];
-    uint32_t rp[kRowsPD][G::MAXT];
-    auto load_unit = [&](int u, u32x4 (&a)[G::MAXT], uint32_t (&pv)[G::MAXT]) {
+    auto load_unit = [&](int u, u32x4 (&a)[G::MAXT]) {
         const UnitPos up = unit_pos(u);
         const bool live = u < units;
         const int ih0 = 2 * up.oh - 1;
@@ -151,16 +156,13 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
 #pragma unroll
         for (int q = 0; q < G::MAXT; ++q) {
             const int ih = ih0 + tk_kh[q];
-            const bool ok = live && tk_valid[q] && (uint32_t)ih < (uint32_t)s.H;
-            const uint32_t off = base + tk_goff[q];
-            a[q] = buf_load16(xr, ok ? off : kOOB);
-            // columns 8 seg - 2, 8 seg - 1 (none left of the row: zero padding)
-            pv[q] = buf_load4(xr, ok && !tk_first[q] ? off - 4u : kOOB);
+            const bool ok = live && tk_load[q] && (uint32_t)ih < (uint32_t)s.H;
+            a[q] = buf_load16(xr, ok ? base + tk_goff[q] : kOOB);
         }
     };
     // Split 8 input columns into the unit's three tap arrays (4 output
     // pixels each) in LDS set `set`.
-    auto write_unit = [&](unsigned char *set, const u32x4 (&a)[G::MAXT], const uint32_t (&pv)[G::MAXT]) {
+    auto write_unit = [&](unsigned char *set, const u32x4 (&a)[G::MAXT]) {
 #pragma unroll
         for (int q = 0; q < G::MAXT; ++q) {
             const u32x4 v = a[q];
@@ -168,7 +170,10 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
             const uint32_t e1 = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
             const uint32_t o0 = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
             const uint32_t o1 = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
-            const uint32_t prev = pv[q];  // high half: column 8 seg - 1
+            // High half: column 8 seg - 1, the last odd column of the lane
+            // below (wave_shr:1); none left of the row: zero padding.
+            uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o1, 0x138, 0xf, 0xf, false);
+            prev = tk_first[q] ? 0u : prev;
             if (!tk_valid[q]) continue;
             unsigned char *dst = set + tk_lds[q];
             *(u32x2 *)(dst) = u32x2{__builtin_amdgcn_perm(o0, prev, 0x05040302u), __builtin_amdgcn_alignbit(o1, o0, 16)};
@@ -211,11 +216,11 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     // unit 0 in wf[0].
     rows_for<0, kRowsPD>([&](auto dc) {
         constexpr int d = decltype(dc)::value;
-        load_unit(d, ra[d], rp[d]);
+        load_unit(d, ra[d]);
     });
     load_w(0, wf[0]);
-    write_unit(sets, ra[0], rp[0]);
-    load_unit(kRowsPD, ra[0], rp[0]);
+    write_unit(sets, ra[0]);
+    load_unit(kRowsPD, ra[0]);
     __syncthreads();
 
     // Unit u: write unit u+1 into set (u+1)%3 and request unit u+1+PD;
@@ -224,8 +229,8 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     // finished before the barrier of unit u-1.
     auto run_unit = [&](int u, auto dc) {
         constexpr int d = decltype(dc)::value;  // (u+1) % 2: register slot of unit u+1 (inputs and weights)
-        write_unit(sets + ((u + 1) % kSets) * G::SET, ra[d], rp[d]);
-        load_unit(u + 1 + kRowsPD, ra[d], rp[d]);
+        write_unit(sets + ((u + 1) % kSets) * G::SET, ra[d]);
+        load_unit(u + 1 + kRowsPD, ra[d]);
         load_w(u + 1, wf[d]);
         __syncthreads();
         const unsigned char *set = sets + (u % kSets) * G::SET;
