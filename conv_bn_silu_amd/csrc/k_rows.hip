@@ -34,8 +34,9 @@
 //    issues the same memory operations in the same order, so the waits
 //    for each unit's data count exactly the operations issued since and
 //    never drain the loads in flight for the units ahead.
-//  * The unit's weights (32 channels x 144 k per wave, 9 fragments of 16
-//    bytes per lane) are loaded one unit ahead into registers.
+//  * Each wave keeps its weights (32 channels x C_in*9 k, 9 fragments of 16
+//    bytes per lane and chunk) in registers for the whole kernel: a unit
+//    issues no weight loads.
 //  * Row pitch in LDS: 2*OW bytes, an odd multiple of 64 for OW = 32*NB
 //    with NB odd (and padded to one otherwise), so the four rows a 16-lane
 //    group reads fall in distinct quarters of the 64 banks.
@@ -182,18 +183,19 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
         }
     };
 
-    // Weights of a unit: lane holds output channel co_lane and, for MFMA
-    // step ks (0..8), k = chunk*144 + 16*ks + 8*(lane>>5) .. +7 (the OIHW row
-    // of w restricted to the chunk's channels is contiguous).
+    // Weights: lane holds output channel co_lane and, for chunk c and MFMA
+    // step ks (0..8), k = c*144 + 16*ks + 8*(lane>>5) .. +7 (the OIHW row of
+    // w restricted to the chunk's channels is contiguous).
     const int co_lane = ct * kRowsTile + wave * 32 + (lane & 31);
-    u32x4 wf[2][9];
-    auto load_w = [&](int u, u32x4 (&f)[9]) {
-        const UnitPos up = unit_pos(u);
-        const bool ok = u < units && co_lane < s.C_out;
-        const uint32_t base = (uint32_t)(co_lane * s.K + up.chunk * kKRows + 8 * (lane >> 5)) * 2u;
+    u32x4 wres[NCH][9];
+    {
+        const bool ok = co_lane < s.C_out;
+        const uint32_t base = (uint32_t)(co_lane * s.K + 8 * (lane >> 5)) * 2u;
 #pragma unroll
-        for (int ks = 0; ks < 9; ++ks) f[ks] = buf_load16(wr, ok ? base + 32u * ks : kOOB);
-    };
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+            for (int ks = 0; ks < 9; ++ks) wres[c][ks] = buf_load16(wr, ok ? base + 2u * (c * kKRows + 16 * ks) : kOOB);
+    }
 
     const float sc = co_lane < s.C_out ? scale[co_lane] : 0.f;
     const float bi = co_lane < s.C_out ? bias[co_lane] : 0.f;
@@ -212,29 +214,26 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
 
-    // Prologue: units 0..PD-1 in flight; unit 0 written to set 0; weights of
-    // unit 0 in wf[0].
+    // Prologue: units 0..PD-1 in flight; unit 0 written to set 0.
     rows_for<0, kRowsPD>([&](auto dc) {
         constexpr int d = decltype(dc)::value;
         load_unit(d, ra[d]);
     });
-    load_w(0, wf[0]);
     write_unit(sets, ra[0]);
     load_unit(kRowsPD, ra[0]);
     __syncthreads();
 
-    // Unit u: write unit u+1 into set (u+1)%3 and request unit u+1+PD;
-    // request unit u+1's weights; barrier; then compute unit u from set u%3.
+    // Unit u (chunk ch): write unit u+1 into set (u+1)%3 and request unit
+    // u+1+PD; barrier; then compute unit u from set u%3.
     // The set written in unit u was last read in unit u-2, which every wave
     // finished before the barrier of unit u-1.
-    auto run_unit = [&](int u, auto dc) {
-        constexpr int d = decltype(dc)::value;  // (u+1) % 2: register slot of unit u+1 (inputs and weights)
+    auto run_unit = [&](int u, auto dc, auto chc) {
+        constexpr int d = decltype(dc)::value;  // (u+1) % 2: register slot of unit u+1
         write_unit(sets + ((u + 1) % kSets) * G::SET, ra[d]);
         load_unit(u + 1 + kRowsPD, ra[d]);
-        load_w(u + 1, wf[d]);
         __syncthreads();
         const unsigned char *set = sets + (u % kSets) * G::SET;
-        const u32x4(&wcurf)[9] = wf[1 - d];
+        const u32x4(&wcurf)[9] = wres[decltype(chc)::value];
         // The fragments of step ks+1 are read while the NB matrix
         // instructions of step ks run (two fragment sets).
         bf16x8 af[2][NB];
@@ -284,7 +283,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     for (int it = 0; it < iters; ++it) {
         rows_for<0, UPI>([&](auto cc) {
             constexpr int c = decltype(cc)::value;
-            run_unit(it * UPI + c, std::integral_constant<int, (c + 1) % 2>{});
+            run_unit(it * UPI + c, std::integral_constant<int, (c + 1) % 2>{}, std::integral_constant<int, c % NCH>{});
             if constexpr (c % NCH == NCH - 1) epilogue(it * RPI + c / NCH);
         });
     }
