@@ -40,8 +40,11 @@
 //  * Row pitch in LDS: 2*OW bytes, an odd multiple of 64 for OW = 32*NB
 //    with NB odd (and padded to one otherwise), so the four rows a 16-lane
 //    group reads fall in distinct quarters of the 64 banks.
-//  * Epilogue after a row's last chunk: folded BN + SiLU, bf16, 8-byte
-//    stores of 4 consecutive pixels of one channel.
+//  * Epilogue after a row's last chunk: folded BN + SiLU, bf16.  A lane
+//    holds 4-pixel groups of one channel and its partner 32 lanes away the
+//    groups beside them; the two swap one group each (ds_bpermute), so that
+//    each stores 16-byte pieces of 8 consecutive pixels (8-byte pieces of 4
+//    when OW is not a multiple of 8).
 #include <type_traits>
 
 #include "cbs_device.h"
@@ -84,8 +87,8 @@ struct RowsGeo {
     static constexpr int MAXT = ((TASKS + 62) / 63 + kRowsWaves - 1) / kRowsWaves;
 };
 
-// NCH: 16-channel chunks of C_in (C_in = 16 * NCH).
-template <int NB, int NCH, int EPI>
+// NCH: 16-channel chunks of C_in (C_in = 16 * NCH); W8: OW % 8 == 0.
+template <int NB, int NCH, bool W8, int EPI>
 __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ scale,
     const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int co_tiles, int ranks_per_xcd,
@@ -263,17 +266,38 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
         const UnitPos up = unit_pos(t * nchunks);
         const uint32_t obase = (uint32_t)(((up.n * s.C_out + co_lane) * s.OH + up.oh) * s.OW) * 2u;
         const bool cok = co_lane < s.C_out && t < steps;
+        const int hl = lane >> 5, partner = 4 * (lane ^ 32);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
+            u32x2 g[4];  // group q: pixels 32b + 8q + 4*hl .. +3
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int px = 32 * b + 8 * q + 4 * (lane >> 5);
                 float o[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     o[r] = EPI == kFused ? bn_silu(acc[b][4 * q + r], sc, bi) : acc[b][4 * q + r];
-                const bool ok = cok && px < s.OW;
-                buf_store8(yr, ok ? obase + 2u * px : kOOB, u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
+                g[q] = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            }
+            if constexpr (W8) {
+                // Pair p: the lower half-wave keeps group 2p and takes the
+                // partner's (pixels 8(2p) + 4 .. +7); the upper keeps group
+                // 2p+1 and takes the partner's (pixels 8(2p+1) .. +3).
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const u32x2 send = hl ? g[2 * p] : g[2 * p + 1];
+                    const u32x2 recv{(uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)send.x),
+                                     (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)send.y)};
+                    const u32x4 v = hl ? u32x4{recv.x, recv.y, g[2 * p + 1].x, g[2 * p + 1].y}
+                                       : u32x4{g[2 * p].x, g[2 * p].y, recv.x, recv.y};
+                    const int px = 32 * b + 8 * (2 * p + hl);
+                    buf_store16(yr, cok && px < s.OW ? obase + 2u * px : kOOB, v);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int px = 32 * b + 8 * q + 4 * hl;
+                    buf_store8(yr, cok && px < s.OW ? obase + 2u * px : kOOB, g[q]);
+                }
             }
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
@@ -289,7 +313,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     }
 }
 
-template <int NB, int NCH, int EPI>
+template <int NB, int NCH, bool W8, int EPI>
 hipError_t launch_rows_t(const Shape &s, const void *x, const void *w, const float *scale, const float *bias,
                          void *y, hipStream_t st, int num_cu) {
     const int co_tiles = (s.C_out + kRowsTile - 1) / kRowsTile;
@@ -297,7 +321,7 @@ hipError_t launch_rows_t(const Shape &s, const void *x, const void *w, const flo
     int n_ranks = (num_cu + co_tiles - 1) / co_tiles;
     if (n_ranks > rows_total) n_ranks = rows_total;
     const int ranks_per_xcd = (n_ranks + 7) / 8;
-    hipLaunchKernelGGL((rows_bf16<NB, NCH, EPI>), dim3(ranks_per_xcd * 8 * co_tiles), dim3(kRowsThreads), 0, st,
+    hipLaunchKernelGGL((rows_bf16<NB, NCH, W8, EPI>), dim3(ranks_per_xcd * 8 * co_tiles), dim3(kRowsThreads), 0, st,
                        (const uint16_t *)x, (const uint16_t *)w, scale, bias, (uint16_t *)y, s, co_tiles,
                        ranks_per_xcd, n_ranks);
     return hipGetLastError();
@@ -318,10 +342,14 @@ bool rows_pointers_ok(const void *x, const void *w, const void *y) {
 
 hipError_t launch_rows(const Shape &s, int epi, const void *x, const void *w, const float *scale, const float *bias,
                        void *y, hipStream_t st, int num_cu) {
-#define CBS_ROWS2(NB_, NCH_)                                                                           \
-    if (s.C_in == kChunk * NCH_)                                                                       \
-        return epi == kFused ? launch_rows_t<NB_, NCH_, kFused>(s, x, w, scale, bias, y, st, num_cu)   \
-                             : launch_rows_t<NB_, NCH_, kConvOnly>(s, x, w, scale, bias, y, st, num_cu);
+#define CBS_ROWS3(NB_, NCH_, W8_)                                                                          \
+    return epi == kFused ? launch_rows_t<NB_, NCH_, W8_, kFused>(s, x, w, scale, bias, y, st, num_cu)      \
+                         : launch_rows_t<NB_, NCH_, W8_, kConvOnly>(s, x, w, scale, bias, y, st, num_cu);
+#define CBS_ROWS2(NB_, NCH_)                                                                               \
+    if (s.C_in == kChunk * NCH_) {                                                                         \
+        if (s.OW % 8 == 0) CBS_ROWS3(NB_, NCH_, true)                                                      \
+        CBS_ROWS3(NB_, NCH_, false)                                                                        \
+    }
 #define CBS_ROWS(NB_)                                                                                  \
     if (s.OW <= RowsGeo<NB_>::OWMAX) {                                                                 \
         CBS_ROWS2(NB_, 1) CBS_ROWS2(NB_, 2) CBS_ROWS2(NB_, 3) CBS_ROWS2(NB_, 4)                        \
@@ -330,6 +358,7 @@ hipError_t launch_rows(const Shape &s, int epi, const void *x, const void *w, co
     CBS_ROWS(1) CBS_ROWS(3) CBS_ROWS(5)
 #undef CBS_ROWS
 #undef CBS_ROWS2
+#undef CBS_ROWS3
     return hipErrorInvalidValue;
 }
 
