@@ -95,6 +95,9 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     int n_ranks) {
     using G = RowsGeo<NB>;
     __shared__ __attribute__((aligned(16))) unsigned char sets[kSets * G::SET];
+    // Target of the staging writes of idle lanes, so that the writes need no
+    // branch and can be scheduled among the matrix instructions.
+    __shared__ __attribute__((aligned(16))) unsigned char sink[2 * G::P + 8];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int j, ct;
@@ -178,8 +181,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
             // below (wave_shr:1); none left of the row: zero padding.
             uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o1, 0x138, 0xf, 0xf, false);
             prev = tk_first[q] ? 0u : prev;
-            if (!tk_valid[q]) continue;
-            unsigned char *dst = set + tk_lds[q];
+            unsigned char *dst = tk_valid[q] ? set + tk_lds[q] : sink;
             *(u32x2 *)(dst) = u32x2{__builtin_amdgcn_perm(o0, prev, 0x05040302u), __builtin_amdgcn_alignbit(o1, o0, 16)};
             *(u32x2 *)(dst + G::P) = u32x2{e0, e1};
             *(u32x2 *)(dst + 2 * G::P) = u32x2{o0, o1};
@@ -224,17 +226,17 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     });
     write_unit(sets, ra[0]);
     load_unit(kRowsPD, ra[0]);
-    __syncthreads();
 
-    // Unit u (chunk ch): write unit u+1 into set (u+1)%3 and request unit
-    // u+1+PD; barrier; then compute unit u from set u%3.
-    // The set written in unit u was last read in unit u-2, which every wave
-    // finished before the barrier of unit u-1.
+    // Unit u (chunk ch): barrier; then write unit u+1 into set (u+1)%3,
+    // request unit u+1+PD and compute unit u from set u%3, all in one stretch
+    // so that the staging work runs beside the matrix instructions.  Set u%3
+    // was written before this barrier; set (u+1)%3 was last read in unit
+    // u-2, which every wave finished before the barrier of unit u-1.
     auto run_unit = [&](int u, auto dc, auto chc) {
         constexpr int d = decltype(dc)::value;  // (u+1) % 2: register slot of unit u+1
+        __syncthreads();
         write_unit(sets + ((u + 1) % kSets) * G::SET, ra[d]);
         load_unit(u + 1 + kRowsPD, ra[d]);
-        __syncthreads();
         const unsigned char *set = sets + (u % kSets) * G::SET;
         const u32x4(&wcurf)[9] = wres[decltype(chc)::value];
         // The fragments of step ks+1 are read while the NB matrix
