@@ -14,8 +14,9 @@
 //    holds channels 32w .. 32w+31 for 7 blocks of 32 pixels.  It sweeps the
 //    input channels in blocks of 32, reading 2L contiguous bytes of each
 //    plane; the workgroups of one XCD hold neighbouring ranges.
-//  * The weights of a wave (32 channels x C_in) sit in VGPRs for the whole
-//    kernel: the B operand of every MFMA, 16 bytes per lane each.
+//  * The weight tile (256 channels x C_in) is staged once in LDS; per block
+//    of 32 input channels each lane reads its two B fragments (16 bytes
+//    each) into registers.
 //  * x blocks are loaded with 16-byte loads (8 pixels of one channel) two
 //    blocks ahead, and stored unchanged to LDS as [channel][pixel] rows with
 //    a pitch of 448 bytes (an odd multiple of 64); the A fragments (8
