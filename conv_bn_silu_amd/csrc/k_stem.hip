@@ -24,8 +24,10 @@
 //    array A_kw[ow] = x[ih][2*ow + kw - 1] (zero outside the row).  Built
 //    from 16-byte loads of 8 input columns, split into even and odd columns
 //    with byte permutes; the kw = 0 array is the odd columns shifted by one,
-//    whose first element comes from the lane holding the previous 8 columns
-//    (a cross-lane permute; lane 0 fetches those 4 bytes itself).
+//    whose first element comes from the lane holding the previous 8 columns:
+//    a wave-wide load covers 63 new segments in lanes 1..63 and repeats the
+//    one before them in lane 0, and each lane takes the column from the
+//    lane below by a DPP wave shift.
 //  * The MFMA A fragment (16 pixels x 8 consecutive k per lane group) is two
 //    ds_read_b64_tr_b16 reads of four k-rows each: k = (ci, kh, kw) picks the
 //    array of input row 2*oh - 1 + kh, channel ci, tap kw; k >= 9*C_in reads
@@ -72,8 +74,9 @@ struct StemGeo {
     static constexpr int SLOT = 9 * P + 64;    // bytes per input row: 3 channels x 3 taps
     static constexpr int RINGB = kRing * SLOT; // the zero row follows the ring
     static constexpr int SP = 16 * NBW + 8;    // staging pitch (elements) per channel row
-    // 16-byte copy tasks per thread per step: 3 rows x 3 channels x W/8.
-    static constexpr int MAXT = (3 * 3 * (2 * OWMAX / 8) + kStemThreads - 1) / kStemThreads;
+    // 16-byte copy tasks per thread per step: 3 rows x 3 channels x W/8,
+    // 63 new ones per wave-wide load.
+    static constexpr int MAXT = ((3 * 3 * (2 * OWMAX / 8) + 62) / 63 + kStemWaves - 1) / kStemWaves;
 };
 
 template <int NBW, int EPI>
@@ -100,31 +103,32 @@ __global__ __launch_bounds__(kStemThreads, 2) void stem_bf16(
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.C_in * s.H * s.W * 2u);
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)s.N * s.C_out * s.OHW * 2u);
 
-    // Copy task q of this thread, task index tid + q*threads, is (input row
-    // kh of the step -- input row 2*oh - 1 + kh --, channel ci, 8-column
-    // segment seg).  Its place in x and in LDS is fixed but for the step.
-    // Consecutive lanes hold consecutive segments of one row unless seg == 0.
+    // Copy task q of this thread, task index t = 63 (4 q + wave) + lane - 1,
+    // is (input row kh of the step -- input row 2*oh - 1 + kh --, channel
+    // ci, 8-column segment seg).  Its place in x and in LDS is fixed but for
+    // the step.  Consecutive lanes hold consecutive segments of one row
+    // unless seg == 0; lane 0 holds the segment before lane 1's and is only
+    // loaded.
     int tk_rr[G::MAXT], tk_lds[G::MAXT];
     uint32_t tk_goff[G::MAXT];
-    bool tk_valid[G::MAXT], tk_first[G::MAXT];
+    bool tk_load[G::MAXT], tk_valid[G::MAXT], tk_first[G::MAXT];
 #pragma unroll
     for (int q = 0; q < G::MAXT; ++q) {
-        const int t = tid + q * kStemThreads;
+        const int traw = 63 * (q * kStemWaves + wave) + lane - 1;
+        const int t = traw < 0 ? 0 : traw;
         const int rr = t / (s.C_in * segs), rem = t - rr * (s.C_in * segs);
         const int ci = rem / segs, seg = rem - ci * segs;
-        tk_valid[q] = t < tasks;
+        tk_load[q] = traw >= 0 && t < tasks;
+        tk_valid[q] = lane > 0 && t < tasks;
         tk_first[q] = seg == 0;
         tk_rr[q] = rr;
         tk_goff[q] = (uint32_t)((ci * s.H + rr) * s.W + 8 * seg) * 2u;
         tk_lds[q] = rr * G::SLOT + ci * 3 * G::P + 8 * seg;
     }
-    const int prev_lane_addr = 4 * ((lane + 63) & 63);
 
-    // ra: x[8 seg .. 8 seg + 7]; rp: x[8 seg - 2 .. 8 seg - 1], fetched only
-    // by lane 0 (other lanes take it from their left neighbour).
+    // ra: x[8 seg .. 8 seg + 7].
     u32x4 ra[kStemPD][G::MAXT];
-    uint32_t rp[kStemPD][G::MAXT];
-    auto load_step = [&](int t, u32x4 (&a)[G::MAXT], uint32_t (&pv)[G::MAXT]) {
+    auto load_step = [&](int t, u32x4 (&a)[G::MAXT]) {
         const int row = j + t * gsz;  // uniform
         const int nn = row / s.OH, oh = row - nn * s.OH;
         const bool live = t < steps;
@@ -134,16 +138,14 @@ __global__ __launch_bounds__(kStemThreads, 2) void stem_bf16(
 #pragma unroll
         for (int q = 0; q < G::MAXT; ++q) {
             const int ih = ih0 + tk_rr[q];
-            const bool ok = live && tk_valid[q] && (uint32_t)ih < (uint32_t)s.H;
-            const uint32_t off = base + tk_goff[q];
-            a[q] = buf_load16(xr, ok ? off : kOOB);
-            pv[q] = buf_load4(xr, ok && lane == 0 && !tk_first[q] ? off - 4u : kOOB);
+            const bool ok = live && tk_load[q] && (uint32_t)ih < (uint32_t)s.H;
+            a[q] = buf_load16(xr, ok ? base + tk_goff[q] : kOOB);
         }
     };
     // Scatter step t's rows into its slot set: per (row, channel, segment)
     // the even columns (kw = 1), odd columns (kw = 2) and the odd columns one
     // to the left (kw = 0), 4 output pixels each.
-    auto write_step = [&](int t, const u32x4 (&a)[G::MAXT], const uint32_t (&pv)[G::MAXT]) {
+    auto write_step = [&](int t, const u32x4 (&a)[G::MAXT]) {
         char *const set = ring + (t % 3) * 3 * G::SLOT;
 #pragma unroll
         for (int q = 0; q < G::MAXT; ++q) {
@@ -152,10 +154,9 @@ __global__ __launch_bounds__(kStemThreads, 2) void stem_bf16(
             const uint32_t e1 = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
             const uint32_t o0 = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
             const uint32_t o1 = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
-            // Column 8 seg - 1 sits in the upper half of the left neighbour's
-            // o1 (or of lane 0's own fetch); zero at the row start.
-            uint32_t prev = (uint32_t)__builtin_amdgcn_ds_bpermute(prev_lane_addr, (int)o1);
-            prev = lane == 0 ? pv[q] : prev;
+            // Column 8 seg - 1 sits in the upper half of the o1 of the lane
+            // below (wave_shr:1); zero at the row start.
+            uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o1, 0x138, 0xf, 0xf, false);
             prev = tk_first[q] ? 0u : prev;
             if (!tk_valid[q]) continue;
             char *dst = set + tk_lds[q];
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(kStemThreads, 2) void stem_bf16(
 
     unroll<0, kStemPD>([&](auto bc) {
         constexpr int b = decltype(bc)::value;
-        load_step(b, ra[b], rp[b]);
+        load_step(b, ra[b]);
     });
 
     // Transposed-read geometry of the 16x16x32 A operand: lane l holds pixel
@@ -206,8 +207,8 @@ __global__ __launch_bounds__(kStemThreads, 2) void stem_bf16(
     const float sc = co < s.C_out ? scale[co] : 0.f, bi = co < s.C_out ? bias[co] : 0.f;
     const float sn = sc * -1.4426950408889634f, bn = bi * -1.4426950408889634f;
 
-    write_step(0, ra[0], rp[0]);
-    load_step(kStemPD, ra[0], rp[0]);
+    write_step(0, ra[0]);
+    load_step(kStemPD, ra[0]);
 
     // This wave's blocks: block gb = wave*NBW + bb of a row starts at column
     // 16*gb; blocks past bpr are idle (they read block 0, store nothing).
@@ -280,21 +281,21 @@ __global__ __launch_bounds__(kStemThreads, 2) void stem_bf16(
         __builtin_amdgcn_wave_barrier();
     };
 
-    // Step t: scatter step t+1's rows (loaded kStemPD steps earlier) into
-    // slot set (t+1) mod 3, request step t+1+kStemPD's rows into the freed
-    // registers, barrier (step t's rows, written last step, become
-    // visible), then compute output row j + t*G.  The set written here was
-    // last read in step t-2, which every wave finished before the previous
-    // barrier.
+    // Step t: barrier (step t's rows, written last step, become visible),
+    // then scatter step t+1's rows (loaded kStemPD steps earlier) into slot
+    // set (t+1) mod 3, request step t+1+kStemPD's rows into the freed
+    // registers and compute output row j + t*G, so the scatter can run
+    // beside the step's arithmetic.  The set written here was last read in
+    // step t-2, which every wave finished before the previous barrier.
     for (int t0 = 0; t0 < steps; t0 += kStemPD) {
         unroll<0, kStemPD>([&](auto dc) {
             constexpr int d = decltype(dc)::value;
             constexpr int slot = (d + 1) % kStemPD;
             const int t = t0 + d;
             if (t >= steps) return;
-            write_step(t + 1, ra[slot], rp[slot]);
-            load_step(t + 1 + kStemPD, ra[slot], rp[slot]);
             __syncthreads();
+            write_step(t + 1, ra[slot]);
+            load_step(t + 1 + kStemPD, ra[slot]);
             compute(t);
         });
     }
