@@ -15,6 +15,13 @@ gpurun_out/).
       profiles/traffic_<workload>.md, which bench.py reads back while the
       kernel sources are unchanged.
 
+  python3 bench_profile.py mfma    [--workload c5]
+      one counter run (SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16)
+      over the bench command; writes
+      profiles/mfma_<workload>.md with the matrix-core busy fraction of the
+      operator's kernel and the MFMA work it counted against the layer's
+      algorithmic FLOP.
+
 This process never touches the GPU itself: rocprofv3 starts bench.py as a
 child.
 """
@@ -108,16 +115,18 @@ def do_trace(args) -> None:
     print(f"[profile] wrote {path}", flush=True)
 
 
-def counter_by_kernel(path: str, counter: str, match) -> dict[str, list[float]]:
+def counter_by_kernel(path: str, counter: str, match, combine=lambda a, b: a + b) -> dict[str, list[float]]:
     """Per kernel name that `match` accepts: the counter's value for each of
-    its dispatches."""
+    its dispatches, the rows of one dispatch (one per hardware instance)
+    combined by `combine` (summed by default)."""
     by: dict[str, dict[str, float]] = {}
     for r in read_csv(path):
         if r["Counter_Name"] != counter or not match(r["Kernel_Name"]):
             continue
         d = by.setdefault(r["Kernel_Name"], {})
         key = r.get("Dispatch_Id") or r.get("Correlation_Id") or str(len(d))
-        d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
+        v = float(r["Counter_Value"])
+        d[key] = combine(d[key], v) if key in d else v
     if not by:
         raise SystemExit(f"no {counter} rows in {path}")
     return {k: list(v.values()) for k, v in by.items()}
@@ -188,15 +197,65 @@ def do_traffic(args) -> None:
     print(f"[profile] wrote {path}: {json.dumps(rec)}", flush=True)
 
 
+def do_mfma(args) -> None:
+    counters = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+    out = os.path.join(RAW, f"{args.workload}_mfma")
+    c = ["rocprofv3", "--pmc"] + counters + ["--output-format", "csv", "-d", out, "-o", "run", "--"] + \
+        bench_cmd(args.workload, 20, ("--no-cpu-baseline",))
+    run(c, 60)
+    path = os.path.join(out, "run_counter_collection.csv")
+    vals = {}
+    for ctr in counters:
+        by = counter_by_kernel(path, ctr, lambda k: "cbs" in k)
+        name = max(by, key=lambda n: sum(by[n]))
+        vals[ctr] = (name, mean(by[name]), len(by[name]))
+    kname = vals[counters[0]][0]
+    durs = {}
+    for r in read_csv(path):
+        if r["Kernel_Name"] == kname and r["Counter_Name"] == counters[0]:
+            durs[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    dur = mean(list(durs.values()))
+    from conv_bn_silu_amd import synth
+    wl = synth.WORKLOADS[args.workload]
+    simds, clock = 4 * 256, 2.4e9
+    busy, mops = vals[counters[0]][1], vals[counters[1]][1]
+    rec = {"workload": wl.name, "kernel": kname[:100], "dispatches": vals[counters[0]][2],
+           "SQ_VALU_MFMA_BUSY_CYCLES": busy, "SQ_INSTS_VALU_MFMA_MOPS_BF16": mops,
+           "mfma_busy_cycles_per_simd": round(busy / simds), "dispatch_duration_us": round(dur * 1e6, 3),
+           "mfma_busy_pct": round(100.0 * busy / simds / (dur * clock), 2),
+           "mfma_flop_counted": mops * 512, "algorithmic_flop": wl.flops,
+           "counted_over_algorithmic": round(mops * 512 / wl.flops, 4),
+           "kernel_sources_digest": __import__("bench").kernel_sources_digest()}
+    text = [f"# Matrix-core use: fused conv+BN+SiLU, workload {wl.name}", "",
+            "Counter run (from the repository root, on one MI355X):", "", "```",
+            " ".join(["timeout -s KILL 60"] + c).replace(out, f"gpurun_out/rocprof/{args.workload}_mfma"), "```", "",
+            "Per-dispatch means for the operator's kernel, SQ counters summed over the chip.  "
+            f"mfma_busy_pct = SQ_VALU_MFMA_BUSY_CYCLES / {simds} SIMDs / (dispatch duration x 2.4 GHz) x 100, "
+            "the duration from the dispatch's own timestamps in the same run (GRBM_GUI_ACTIVE is not used: "
+            "under counter collection it also counts the time around each dispatch).  "
+            "mfma_flop_counted = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 against the layer's 2*M*C_out*K "
+            "(tile padding makes it larger).", "",
+            "```json", json.dumps(rec, indent=1), "```", ""]
+    os.makedirs(args.out, exist_ok=True)
+    dst = os.path.join(args.out, f"mfma_{wl.name}.md")
+    with open(dst, "w") as f:
+        f.write("\n".join(text))
+    print(f"[profile] wrote {dst}: {json.dumps(rec)}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("mode", choices=["trace", "traffic"])
+    ap.add_argument("mode", choices=["trace", "traffic", "mfma"])
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--out", default=PROFILES, help="where the summaries go (default profiles/)")
     args = ap.parse_args()
     os.makedirs(RAW, exist_ok=True)
     if args.mode == "trace":
         do_trace(args)
+    elif args.mode == "mfma":
+        if args.workload == "c2" and "--workload" not in sys.argv:
+            args.workload = "c5"
+        do_mfma(args)
     else:
         do_traffic(args)
 
