@@ -14,6 +14,10 @@ traffic counted by rocprofv3 (when the committed counter record matches the
 current kernel sources), and the CPU oracle timed on a bounded sample of the
 same workload on the host cores.
 
+The line also carries "ceilings": the rate a plain 1 GiB device copy reaches
+on the same GPU (the practical ceiling of the streaming layers; per layer,
+"frac_of_copy" sets the layer's algorithmic GB/s against it).
+
 Extra figures (each adds a key to the same line):
   --layers    the fused operator on all five workloads
   --unfused   the three-kernel sequence conv -> t1 -> BN -> t2 -> SiLU -> y
@@ -231,6 +235,32 @@ def cpu_baseline(key: str, min_seconds: float = 12.0, max_reps: int = 200) -> di
                       f"SiLU passes, {t_total:.1f} s on {threads} threads"}
 
 
+def copy_ceiling(mib: int = 1024, reps: int = 20) -> dict:
+    """The HBM rate a plain device-to-device copy of `mib` MiB reaches on
+    this GPU (read + write bytes over the time of `reps` back-to-back
+    copies, HIP events on the copying stream): the practical ceiling for
+    the streaming layers, reported beside the 8 TB/s peak."""
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(2 * n / sec / 1e9, 1), "copy_bytes_each_way": n,
+            "what": "torch device-to-device copy, read + write bytes per second"}
+
+
 def copy_calibration(mib: int, reps: int) -> None:
     """A plain device-to-device copy of a known size, for scaling the HBM
     byte counters (run under rocprofv3 --pmc)."""
@@ -296,6 +326,9 @@ def main():
                    "algorithmic_bytes": wl.algorithmic_bytes, "flops": wl.flops},
         "roofline": roof,
     }
+    ceil = copy_ceiling()
+    log(f"[bench] copy ceiling: {ceil['copy_gbs']:.0f} GB/s")
+    out["ceilings"] = ceil
     sub_steps = max(20, args.steps // 2)
     if args.layers or args.unfused or args.variants:
         layers = {}
@@ -308,7 +341,8 @@ def main():
                 ent = {"variant": q["variant"], "kernel_us": round(q["kernel_us_mean"], 3),
                        "tflops": round(q["tflops_kernel"], 3),
                        "hbm_gbs_algorithmic": round(q["hbm_gbs_alg"], 1),
-                       "bound": q["roofline"]["bound"], "frac": q["roofline"]["frac"]}
+                       "bound": q["roofline"]["bound"], "frac": q["roofline"]["frac"],
+                       "frac_of_copy": round(q["hbm_gbs_alg"] / ceil["copy_gbs"], 4)}
                 log(f"[bench] layer {key}: {q['kernel_us_mean']:.2f} us ({q['variant']})")
             if args.unfused:
                 u = measure_unfused(key, sub_steps, args.warmup)
