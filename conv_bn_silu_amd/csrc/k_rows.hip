@@ -23,7 +23,9 @@
 //  * A unit is (output row, 16-channel chunk): its 48 input row segments
 //    are loaded two units ahead into registers (16-byte loads of 8 columns,
 //    split into even and odd columns with byte permutes), written to one of
-//    three LDS sets one unit ahead, and read by the unit after a barrier.
+//    three LDS sets during the unit before the one that reads it (after
+//    that unit's barrier, beside its matrix work), and read after the next
+//    barrier.
 //    The shifted odd array needs the column left of each segment: a wave's
 //    load covers 63 consecutive segments in lanes 1..63 and repeats the one
 //    before them in lane 0, so every lane takes that column from the lane
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     constexpr int RPI = NCH % 2 == 0 ? 1 : 2;  // output rows per loop iteration
     constexpr int UPI = RPI * NCH;              // units per iteration (even)
     const int iters = (steps + RPI - 1) / RPI;
-    const int units = steps * nchunks;  // units past this one (a padding row) load zeros and store nothing
+    const int units = steps * nchunks;  // units from this index on (a padding row) load zeros, store nothing
     const int segs = s.W / 8;
     const int tasks = 3 * kChunk * segs;
 
