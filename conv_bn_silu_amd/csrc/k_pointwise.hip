@@ -260,11 +260,16 @@ __global__ __launch_bounds__(kThreadsPw, 1) void pointwise_bf16(
 }
 
 // Pixels per range: the M pixels split evenly over one workgroup per CU,
-// rounded up to a multiple of 8, at most 224 and at most one image.
+// rounded up to a multiple of 8, at most 224 and at most one image.  When
+// every CU would get at least 3/4 of a full range, full ranges are used
+// instead (fewer, longer workgroups: the 1x1 layer at N=8, 256 -> 256,
+// 80x80 runs 1.7% faster with 229 ranges of 224 pixels than with 256 of
+// 200, measured).
 int range_len(const Shape &s, int num_cu) {
     const int co_tiles = (s.C_out + kTileCo - 1) / kTileCo;
     const int per = (int)(((int64_t)s.M * co_tiles + num_cu - 1) / num_cu);
     int L = (per + 7) / 8 * 8;
+    if (4 * L >= 3 * kMaxL) L = kMaxL;
     if (L > kMaxL) L = kMaxL;
     if (L > s.HW) L = s.HW;
     if (L < 8) L = 8;

@@ -61,6 +61,9 @@ SWEEP = [
     (5, 256, 8, 8, 16, 1, 1, 1, 0),
     (1, 8, 1, 8, 1, 1, 1, 1, 0),
     (7, 128, 12, 12, 200, 1, 1, 1, 0),
+    # enough pixels for full 224-pixel ranges: ranges across image
+    # boundaries and a short last range
+    (11, 16, 64, 64, 24, 1, 1, 1, 0),
     # stems for the small-K variant: odd output-row counts, 1-3 channels,
     # C_out below 16, each row width class, more images than compute units
     (2, 3, 18, 64, 16, 3, 3, 2, 1),
