@@ -19,7 +19,9 @@ on the same GPU (the practical ceiling of the streaming layers; per layer,
 "frac_of_copy" sets the layer's algorithmic GB/s against it).
 
 Extra figures (each adds a key to the same line):
-  --layers    the fused operator on all five workloads
+  --layers    the fused operator on all five workloads (per layer: time, TFLOP/s,
+              algorithmic GB/s, the bound and its fraction, and both the
+              fraction of the matrix peak and of the HBM peak)
   --unfused   the three-kernel sequence conv -> t1 -> BN -> t2 -> SiLU -> y
               beside the fused call, per workload
   --variants  every variant that supports each workload, and whether the
@@ -342,7 +344,11 @@ def main():
                        "tflops": round(q["tflops_kernel"], 3),
                        "hbm_gbs_algorithmic": round(q["hbm_gbs_alg"], 1),
                        "bound": q["roofline"]["bound"], "frac": q["roofline"]["frac"],
-                       "frac_of_copy": round(q["hbm_gbs_alg"] / ceil["copy_gbs"], 4)}
+                       "mfma_frac": round(q["tflops_kernel"] / (MFMA_F32_TFLOPS if q["wl"].dtype == 0
+                                                                 else MFMA_BF16_TFLOPS), 4),
+                       "hbm_frac": round(q["hbm_gbs_alg"] / HBM_PEAK_GBS, 4),
+                       "frac_of_copy": round(q["hbm_gbs_alg"] / ceil["copy_gbs"], 4),
+                       "kernel_us_median_launch": round(q["launch_events_us_median"], 3)}
                 log(f"[bench] layer {key}: {q['kernel_us_mean']:.2f} us ({q['variant']})")
             if args.unfused:
                 u = measure_unfused(key, sub_steps, args.warmup)
