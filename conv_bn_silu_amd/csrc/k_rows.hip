@@ -30,23 +30,24 @@
 //    load covers 63 consecutive segments in lanes 1..63 and repeats the one
 //    before them in lane 0, so every lane takes that column from the lane
 //    below it by a DPP wave shift (lane 0 only supplies it).
-//  * The loop body is one output row (all its chunks, unrolled; two rows
-//    when the chunk count is odd, so that the register slots of the units
-//    repeat), with the epilogue at a fixed place in it: every iteration
-//    issues the same memory operations in the same order, so the waits
-//    for each unit's data count exactly the operations issued since and
-//    never drain the loads in flight for the units ahead.
+//  * The loop body is two output rows (all their chunks, unrolled), each
+//    with its own set of accumulators: every iteration issues the same
+//    memory operations in the same order, so the waits for each unit's data
+//    count exactly the operations issued since and never drain the loads in
+//    flight for the units ahead.
 //  * Each wave keeps its weights (32 channels x C_in*9 k, 9 fragments of 16
 //    bytes per lane and chunk) in registers for the whole kernel: a unit
 //    issues no weight loads.
 //  * Row pitch in LDS: 2*OW bytes, an odd multiple of 64 for OW = 32*NB
 //    with NB odd (and padded to one otherwise), so the four rows a 16-lane
 //    group reads fall in distinct quarters of the 64 banks.
-//  * Epilogue after a row's last chunk: folded BN + SiLU, bf16.  A lane
-//    holds 4-pixel groups of one channel and its partner 32 lanes away the
-//    groups beside them; the two swap one group each (ds_bpermute), so that
-//    each stores 16-byte pieces of 8 consecutive pixels (8-byte pieces of 4
-//    when OW is not a multiple of 8).
+//  * Epilogue: folded BN + SiLU, bf16, for a row while the next row is
+//    computed into the other accumulator set, in ten pieces placed after the
+//    matrix instructions of chosen steps, so that its arithmetic and stores
+//    fill the gaps between them.  A lane holds 4-pixel groups of one channel
+//    and its partner 32 lanes away the groups beside them; the two swap one
+//    group each (ds_bpermute), so that each stores 16-byte pieces of 8
+//    consecutive pixels (8-byte pieces of 4 when OW is not a multiple of 8).
 #include <type_traits>
 
 #include "cbs_device.h"
@@ -114,9 +115,6 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     if (j >= rows_total) return;  // uniform
     const int steps = (rows_total - j + n_ranks - 1) / n_ranks;  // output rows of this rank
     constexpr int nchunks = NCH;
-    constexpr int RPI = NCH % 2 == 0 ? 1 : 2;  // output rows per loop iteration
-    constexpr int UPI = RPI * NCH;              // units per iteration (even)
-    const int iters = (steps + RPI - 1) / RPI;
     const int units = steps * nchunks;  // units from this index on (a padding row) load zeros, store nothing
     const int segs = s.W / 8;
     const int tasks = 3 * kChunk * segs;
@@ -215,11 +213,17 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     const int grp = lane >> 4, jl = lane & 15;
     const int tr_off = (8 * (grp >> 1) + (jl >> 2)) * G::P + 2 * (16 * (grp & 1) + 4 * (jl & 3));
 
-    f32x16 acc[NB];
+    // Two accumulator sets: the two output rows of a loop iteration use one
+    // each, and the first matrix instruction of a row starts from zero.
+    // While a row is computed, the previous row's epilogue runs from the
+    // other set in ten pieces placed among the matrix instructions.
+    f32x16 accs[2][NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) accs[r][b][e] = 0.f;
 
     // Prologue: units 0..PD-1 in flight; unit 0 written to set 0.
     rows_for<0, kRowsPD>([&](auto dc) {
@@ -229,18 +233,71 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     write_unit(sets, ra[0]);
     load_unit(kRowsPD, ra[0]);
 
-    // Unit u (chunk ch): barrier; then write unit u+1 into set (u+1)%3,
-    // request unit u+1+PD and compute unit u from set u%3, all in one stretch
-    // so that the staging work runs beside the matrix instructions.  Set u%3
-    // was written before this barrier; set (u+1)%3 was last read in unit
-    // u-2, which every wave finished before the barrier of unit u-1.
-    auto run_unit = [&](int u, auto dc, auto chc) {
+    // Piece i of the epilogue of the rank's output row t, from accumulator
+    // set pa (stores dropped for t < 0, before the first row, and for a
+    // padding row t >= steps): pixel block i / 2, groups q = 2p, 2p+1 with
+    // p = i % 2; lane holds channel co_lane, group q pixels
+    // 32b + 8q + 4*(lane>>5) .. +3.  A lane and its partner 32 lanes away
+    // swap one group each (ds_bpermute), so that each stores a 16-byte piece
+    // of 8 consecutive pixels (8-byte pieces of 4 when OW is not a multiple
+    // of 8).
+    constexpr int kPieces = 2 * NB;
+    auto epi_piece = [&](int t, const f32x16 (&pa)[NB], auto ic) {
+        constexpr int i = decltype(ic)::value, b = i / 2, p = i % 2;
+        const bool live = t >= 0 && t < steps;
+        const UnitPos up = unit_pos((live ? t : 0) * nchunks);
+        const uint32_t obase = (uint32_t)(((up.n * s.C_out + co_lane) * s.OH + up.oh) * s.OW) * 2u;
+        const bool cok = co_lane < s.C_out && live;
+        const int hl = lane >> 5;
+        u32x2 g[2];
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            const int q = 2 * p + qq;
+            float o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                o[r] = EPI == kFused ? bn_silu(pa[b][4 * q + r], sc, bi) : pa[b][4 * q + r];
+            g[qq] = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        }
+        if constexpr (W8) {
+            // The lower half-wave keeps group 2p and takes the partner's
+            // (pixels 8(2p) + 4 .. +7); the upper keeps group 2p+1 and takes
+            // the partner's (pixels 8(2p+1) .. +3).
+            const int partner = 4 * (lane ^ 32);
+            const u32x2 send = hl ? g[0] : g[1];
+            const u32x2 recv{(uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)send.x),
+                             (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)send.y)};
+            const u32x4 v = hl ? u32x4{recv.x, recv.y, g[1].x, g[1].y} : u32x4{g[0].x, g[0].y, recv.x, recv.y};
+            const int px = 32 * b + 8 * (2 * p + hl);
+            buf_store16(yr, cok && px < s.OW ? obase + 2u * px : kOOB, v);
+        } else {
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                const int px = 32 * b + 8 * (2 * p + qq) + 4 * hl;
+                buf_store8(yr, cok && px < s.OW ? obase + 2u * px : kOOB, g[qq]);
+            }
+        }
+    };
+
+    // Unit u (chunk ch of the iteration's row rc): barrier; then write unit
+    // u+1 into set (u+1)%3, request unit u+1+PD and compute unit u from set
+    // u%3 into accumulator set rc, all in one stretch so that the staging
+    // work runs beside the matrix instructions.  Set u%3 was written before
+    // this barrier; set (u+1)%3 was last read in unit u-2, which every wave
+    // finished before the barrier of unit u-1.  After step ks of chunk ch
+    // come the epilogue pieces i of the previous row (set 1 - rc) whose slot
+    // floor(i * 9 * NCH / (2 NB)) is ch * 9 + ks: the row's ten pieces are
+    // spread over its units' steps.
+    auto run_unit = [&](int u, auto dc, auto chc, auto rcc) {
         constexpr int d = decltype(dc)::value;  // (u+1) % 2: register slot of unit u+1
+        constexpr int ch = decltype(chc)::value, rc = decltype(rcc)::value;
+        f32x16(&acc)[NB] = accs[rc];
         __syncthreads();
         write_unit(sets + ((u + 1) % kSets) * G::SET, ra[d]);
         load_unit(u + 1 + kRowsPD, ra[d]);
         const unsigned char *set = sets + (u % kSets) * G::SET;
-        const u32x4(&wcurf)[9] = wres[decltype(chc)::value];
+        const u32x4(&wcurf)[9] = wres[ch];
+        const int t_prev = u / nchunks - 1;
         // The fragments of step ks+1 are read while the NB matrix
         // instructions of step ks run (two fragment sets).
         bf16x8 af[2][NB];
@@ -258,63 +315,36 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
             constexpr int ks = decltype(kc)::value;
             if constexpr (ks + 1 < 9) read_step(ks + 1, af[(ks + 1) & 1]);
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][b], __builtin_bit_cast(bf16x8, wcurf[ks]),
-                                                                 acc[b], 0, 0, 0);
+            for (int b = 0; b < NB; ++b) {
+                if constexpr (ch == 0 && ks == 0)
+                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][b], __builtin_bit_cast(bf16x8, wcurf[0]),
+                                                                     f32x16{}, 0, 0, 0);
+                else
+                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        af[ks & 1][b], __builtin_bit_cast(bf16x8, wcurf[ks]), acc[b], 0, 0, 0);
+            }
+            rows_for<0, kPieces>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                if constexpr (i * 9 * NCH / kPieces == ch * 9 + ks) epi_piece(t_prev, accs[1 - rc], ic);
+            });
         });
-    };
-    // Epilogue of the rank's output row t (stores dropped for a padding row
-    // t >= steps): lane holds channel co_lane, pixels
-    // 32b + 8*(i>>2) + 4*(lane>>5) + (i&3).
-    auto epilogue = [&](int t) {
-        const UnitPos up = unit_pos(t * nchunks);
-        const uint32_t obase = (uint32_t)(((up.n * s.C_out + co_lane) * s.OH + up.oh) * s.OW) * 2u;
-        const bool cok = co_lane < s.C_out && t < steps;
-        const int hl = lane >> 5, partner = 4 * (lane ^ 32);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            u32x2 g[4];  // group q: pixels 32b + 8q + 4*hl .. +3
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float o[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    o[r] = EPI == kFused ? bn_silu(acc[b][4 * q + r], sc, bi) : acc[b][4 * q + r];
-                g[q] = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-            }
-            if constexpr (W8) {
-                // Pair p: the lower half-wave keeps group 2p and takes the
-                // partner's (pixels 8(2p) + 4 .. +7); the upper keeps group
-                // 2p+1 and takes the partner's (pixels 8(2p+1) .. +3).
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    const u32x2 send = hl ? g[2 * p] : g[2 * p + 1];
-                    const u32x2 recv{(uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)send.x),
-                                     (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)send.y)};
-                    const u32x4 v = hl ? u32x4{recv.x, recv.y, g[2 * p + 1].x, g[2 * p + 1].y}
-                                       : u32x4{g[2 * p].x, g[2 * p].y, recv.x, recv.y};
-                    const int px = 32 * b + 8 * (2 * p + hl);
-                    buf_store16(yr, cok && px < s.OW ? obase + 2u * px : kOOB, v);
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int px = 32 * b + 8 * q + 4 * hl;
-                    buf_store8(yr, cok && px < s.OW ? obase + 2u * px : kOOB, g[q]);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
-        }
     };
     static_assert(kRowsPD == 2, "register slots alternate with unit parity");
-    for (int it = 0; it < iters; ++it) {
-        rows_for<0, UPI>([&](auto cc) {
+    // Two output rows per iteration (the unit count 2 NCH is even, so the
+    // register slots of the units repeat); a padding row past `steps`
+    // computes on zeros and stores nothing.
+    constexpr int UPI2 = 2 * NCH;
+    const int iters2 = (steps + 1) / 2;
+    for (int it = 0; it < iters2; ++it) {
+        rows_for<0, UPI2>([&](auto cc) {
             constexpr int c = decltype(cc)::value;
-            run_unit(it * UPI + c, std::integral_constant<int, (c + 1) % 2>{}, std::integral_constant<int, c % NCH>{});
-            if constexpr (c % NCH == NCH - 1) epilogue(it * RPI + c / NCH);
+            run_unit(it * UPI2 + c, std::integral_constant<int, (c + 1) % 2>{}, std::integral_constant<int, c % NCH>{},
+                     std::integral_constant<int, c / NCH>{});
         });
     }
+    // The last row computed (row 2*iters2 - 1, in set 1; a padding row if it
+    // is past `steps`) is still pending.
+    rows_for<0, kPieces>([&](auto ic) { epi_piece(2 * iters2 - 1, accs[1], ic); });
 }
 
 template <int NB, int NCH, bool W8, int EPI>
