@@ -1,42 +1,47 @@
 #!/usr/bin/env python3
 """Benchmark of the fused conv2d + folded BN + SiLU operator on one MI355X.
 
-One step = one fused call over the whole layer (one batch of seeded synthetic
-input, already resident in HBM).  The headline workload is the bf16 1x1
-pointwise layer (N=8, 256 -> 256 channels, 80x80); ``--workload`` picks
-another of the five.  Input/output buffer sets are rotated so that the
-working set of consecutive steps exceeds twice the 256 MB Infinity Cache and
-every step streams from HBM.
+One step = one fused call over a whole layer (one batch of seeded synthetic
+input, already resident in HBM).  The headline is the compute-bound deep 3x3
+layer (bf16, N=64, 512 -> 512 channels, 20x20), the layer the metric's
+"% of bf16 MFMA" is about; every run also measures the other four layers and
+reports them under "layers".  Input/output buffer sets are rotated so that
+the working set of consecutive steps exceeds twice the 256 MB Infinity Cache
+and every step streams from HBM.
 
-Prints ONE JSON line with the metric (TFLOP/s), the roofline of the dominant
-kernel measured with HIP events on the stream the kernel runs on, the HBM
-traffic counted by rocprofv3 (when the committed counter record matches the
-current kernel sources), and the CPU oracle timed on a bounded sample of the
-same workload on the host cores.
+Timing: W untimed warm-up steps, then exactly K steps in one timed region,
+bracketed by torch.cuda.synchronize() on both sides, with a HIP event pair on
+the launch stream around the same K launches.  value and ms_per_step come
+from the wall clock of that region; the roofline's "achieved" from the event
+pair (the kernel's average launch duration), so the kernel time per step is
+never above ms_per_step.
 
-The line also carries "ceilings": the rate a plain 1 GiB device copy reaches
-on the same GPU (the practical ceiling of the streaming layers; per layer,
-"frac_of_copy" sets the layer's algorithmic GB/s against it).
+Prints ONE JSON line: the metric (TFLOP/s), the roofline of the dominant
+kernel, the HBM traffic counted by rocprofv3 (when the committed counter
+record matches the current kernel source), the measured ceilings (a
+register-only MFMA loop and a streaming copy, both our own kernels), each
+layer's figures with the unfused three-kernel sequence beside it, and the CPU
+oracle timed on a bounded sample on the host cores.
 
-Extra figures (each adds a key to the same line):
-  --layers    the fused operator on all five workloads (per layer: time, TFLOP/s,
-              algorithmic GB/s, the bound and its fraction, and both the
-              fraction of the matrix peak and of the HBM peak)
-  --unfused   the three-kernel sequence conv -> t1 -> BN -> t2 -> SiLU -> y
-              beside the fused call, per workload
-  --variants  every variant that supports each workload, and whether the
-              automatic dispatch picked the fastest
+Flags:
+  --workload KEY  headline layer (default c5)
+  --only          only the headline layer (no layers, ceilings or CPU
+                  baseline): for profiling runs
+  --variants      also time every variant that supports each layer and a
+                  sweep of shapes on both sides of each dispatch threshold;
+                  exits with status 3 if the automatic choice is more than 5%
+                  slower than the fastest variant on any of them
 Progress goes to stderr; stdout carries only the JSON line.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
-import glob
 import json
 import math
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -48,17 +53,28 @@ MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
 MFMA_F32_TFLOPS = 157.3    # fp32 MFMA
 MALL_BYTES = 256 << 20     # Infinity Cache
 METRIC = "fused conv+BN+SiLU TFLOP/s and % of bf16 MFMA or HBM roofline per layer"
+HEADLINE = "c5"
+DISPATCH_SLACK = 1.05      # AUTO may be at most 5% slower than the fastest variant
+
+# The kernel source each variant runs (plus the shared device headers): a
+# counter record stays valid while these files are unchanged.
+VARIANT_SOURCES = {
+    "gemm_gather": "k_gather.hip", "gemm_window": "k_window.hip", "pointwise": "k_pointwise.hip",
+    "small_k": "k_stem.hip", "scalar": "k_scalar.hip", "gemm_window32": "k_window32.hip",
+    "strided_rows": "k_rows.hip",
+}
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_sources_digest() -> str:
+def kernel_sources_digest(variant: str) -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "conv_bn_silu_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    csrc = os.path.join(ROOT, "conv_bn_silu_amd", "csrc")
+    for name in (VARIANT_SOURCES[variant], "cbs_device.h", "cbs_shape.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -80,12 +96,14 @@ def roofline(wl, seconds: float) -> dict:
 
 class Layer:
     """Device buffers of one workload: `sets` rotated copies of x and y (so
-    consecutive steps do not hit in the Infinity Cache), one w/scale/bias."""
+    consecutive steps do not hit in the Infinity Cache), one w/scale/bias.
+    `extra_outputs` more output-sized buffers per set (t1, t2 of the
+    unfused sequence)."""
 
-    def __init__(self, key: str, extra_outputs: int = 0):
+    def __init__(self, wl, extra_outputs: int = 0):
         import torch
         from conv_bn_silu_amd import synth
-        self.wl = wl = synth.WORKLOADS[key]
+        self.wl = wl
         inp = synth.make_inputs(wl)
         dev = torch.device("cuda", 0)
         if wl.dtype == synth.DTYPE_BF16:
@@ -96,7 +114,7 @@ class Layer:
             self.w = torch.from_numpy(inp.w).to(dev)
         self.sc = torch.from_numpy(inp.scale).to(dev)
         self.bi = torch.from_numpy(inp.bias).to(dev)
-        per_set = wl.algorithmic_bytes * (1 + extra_outputs)
+        per_set = wl.algorithmic_bytes + extra_outputs * wl.N * wl.C_out * wl.OH * wl.OW * wl.elem_bytes
         self.sets = max(2, math.ceil(2 * MALL_BYTES / per_set))
         self.xs = [x0] + [x0.clone() for _ in range(self.sets - 1)]
         shape = (wl.N, wl.C_out, wl.OH, wl.OW)
@@ -105,53 +123,39 @@ class Layer:
         self.geo = (wl.N, wl.C_in, wl.H, wl.W, wl.C_out, wl.KH, wl.KW, wl.stride, wl.pad, wl.dtype)
 
 
-def time_steps(step, steps: int, warmup: int, stream) -> dict:
-    """Wall clock over exactly `steps` steps, then HIP events on the launch
-    stream: one pair around each launch (per-launch kernel duration) and one
-    pair around the whole region."""
+def timed_region(step, steps: int, warmup: int, stream) -> dict:
+    """W warm-up steps, then exactly `steps` steps in one region bracketed by
+    device synchronisation, with a HIP event pair on the launch stream around
+    the same launches."""
     import torch
     for i in range(warmup):
         step(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
         step(i)
+    e1.record(stream)
     issued = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        evs[i][0].record(stream)
-        step(i)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    durs = sorted(a.elapsed_time(b) * 1e-3 for a, b in evs)
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record(stream)
-    for i in range(steps):
-        step(i)
-    r1.record(stream)
-    torch.cuda.synchronize()
-    return {"wall_s": wall, "host_issue_s": issued, "launch_mean_s": sum(durs) / len(durs),
-            "launch_median_s": durs[len(durs) // 2],
-            "launch_min_s": durs[0], "region_per_step_s": r0.elapsed_time(r1) * 1e-3 / steps}
+    return {"wall_s": wall, "events_s": e0.elapsed_time(e1) * 1e-3, "host_issue_s": issued}
 
 
-def measure_fused(key: str, steps: int, warmup: int, variant: str = "auto", layer: Layer | None = None) -> dict:
+def measure_fused(wl, steps: int, warmup: int, variant: str = "auto", layer: Layer | None = None) -> dict:
     import torch
     from conv_bn_silu_amd import binding as B
-    L = layer or Layer(key)
-    wl = L.wl
+    L = layer or Layer(wl)
     lib = B.default_library()
     v = B.VARIANTS[variant]
     if v == 0:
         v = B.select_variant(*L.geo)
     stream = torch.cuda.current_stream(torch.device("cuda", 0))
     sp = stream.cuda_stream
-
     # Arguments bound once per buffer set, and the C entry point called
     # directly: at tens of microseconds per launch the Python side must stay
-    # well ahead of the GPU, or the timing measures the host.
+    # ahead of the GPU, or the timing measures the host.
     fn, handle = B.lib.conv_bn_silu_run_variant, lib.handle
     args = [(handle, v, L.xs[j].data_ptr(), L.w.data_ptr(), L.sc.data_ptr(), L.bi.data_ptr(),
              L.ys[j][0].data_ptr(), *L.geo, sp) for j in range(L.sets)]
@@ -161,31 +165,24 @@ def measure_fused(key: str, steps: int, warmup: int, variant: str = "auto", laye
         if rc:
             lib.run_ptr(*args[i % L.sets][1:])  # raises with the status and HIP error
 
-    t = time_steps(step, steps, warmup, stream)
-    # Average launch duration: HIP events around the whole back-to-back
-    # region on the launch stream, divided by the launch count.  (The
-    # per-launch event pairs are reported too; the event packets between
-    # launches make them read slightly longer.)
-    kern = t["region_per_step_s"]
-    return {"key": key, "wl": wl, "variant": B.variant_name(v), "sets": L.sets,
-            "ms_per_step": t["wall_s"] / steps * 1e3, "tflops": wl.flops / (t["wall_s"] / steps) / 1e12,
-            "kernel_us_mean": kern * 1e6, "host_issue_us_per_step": t["host_issue_s"] / steps * 1e6,
-            "launch_events_us_mean": t["launch_mean_s"] * 1e6,
-            "launch_events_us_median": t["launch_median_s"] * 1e6,
-            "kernel_us_min": t["launch_min_s"] * 1e6, "region_us_per_step": t["region_per_step_s"] * 1e6,
-            "roofline": roofline(wl, kern), "hbm_gbs_alg": wl.algorithmic_bytes / kern / 1e9,
-            "tflops_kernel": wl.flops / kern / 1e12}
+    t = timed_region(step, steps, warmup, stream)
+    kern = t["events_s"] / steps
+    return {"wl": wl, "variant": B.variant_name(v), "sets": L.sets, "steps": steps,
+            "wall_per_step_s": t["wall_s"] / steps, "kernel_s": kern,
+            "host_issue_us_per_step": t["host_issue_s"] / steps * 1e6,
+            "roofline": roofline(wl, kern), "tflops_kernel": wl.flops / kern / 1e12,
+            "tflops_wall": wl.flops / (t["wall_s"] / steps) / 1e12,
+            "hbm_gbs_alg": wl.algorithmic_bytes / kern / 1e9}
 
 
-def measure_unfused(key: str, steps: int, warmup: int) -> dict:
-    """conv -> t1, BN -> t2, SiLU -> y, all three intermediates in HBM."""
+def measure_unfused(wl, steps: int, warmup: int) -> dict:
+    """conv -> t1, BN -> t2, SiLU -> y, the intermediates in HBM."""
     import torch
     from conv_bn_silu_amd import binding as B
-    L = Layer(key, extra_outputs=2)
+    L = Layer(wl, extra_outputs=2)
     lib = B.default_library()
     stream = torch.cuda.current_stream(torch.device("cuda", 0))
     sp = stream.cuda_stream
-
     fn, handle = B.lib.conv_bn_silu_run_unfused, lib.handle
     args = [(handle, L.xs[j].data_ptr(), L.w.data_ptr(), L.sc.data_ptr(), L.bi.data_ptr(),
              L.ys[j][1].data_ptr(), L.ys[j][2].data_ptr(), L.ys[j][0].data_ptr(), *L.geo, sp)
@@ -194,15 +191,15 @@ def measure_unfused(key: str, steps: int, warmup: int) -> dict:
     def step(i):
         rc = fn(*args[i % L.sets])
         if rc:
-            lib.run_unfused_ptr(*args[i % L.sets][1:])  # raises with the status and HIP error
+            lib.run_unfused_ptr(*args[i % L.sets][1:])
 
-    t = time_steps(step, steps, warmup, stream)
-    return {"us_per_step": t["region_per_step_s"] * 1e6, "wall_us_per_step": t["wall_s"] / steps * 1e6}
+    t = timed_region(step, steps, warmup, stream)
+    return {"us_per_step": t["events_s"] / steps * 1e6}
 
 
-def traffic_for(wl) -> dict | None:
+def traffic_for(wl, variant: str) -> dict | None:
     """HBM bytes per launch from the committed rocprofv3 counter record, if it
-    was taken on the current kernel sources."""
+    was taken on the current source of the variant's kernel."""
     path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.md")
     if not os.path.exists(path):
         return None
@@ -211,56 +208,136 @@ def traffic_for(wl) -> dict | None:
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("kernel_sources_digest") != kernel_sources_digest():
+    if rec.get("variant") != variant or rec.get("kernel_sources_digest") != kernel_sources_digest(variant):
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
 
 
-def cpu_baseline(key: str, min_seconds: float = 12.0, max_reps: int = 200) -> dict:
-    """The oracle (unfused fp64 three-pass sequence, as it stands) on the host
-    cores, over the whole workload, repeated until ~min_seconds have passed."""
-    import oracle
-    from conv_bn_silu_amd import synth
-    wl = synth.WORKLOADS[key]
-    inp = synth.make_inputs(wl)
-    o = oracle.get()
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
-    reps, t_total = 0, 0.0
-    while reps < max_reps and (reps == 0 or t_total < min_seconds):
-        t0 = time.perf_counter()
-        o.forward(inp.x, inp.w, inp.scale, inp.bias, wl.stride, wl.pad, nthreads=threads)
-        t_total += time.perf_counter() - t0
-        reps += 1
-    return {"value": round(wl.flops * reps / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"whole workload {wl.name} ({wl.flops / 1e9:.2f} GFLOP) x{reps}, fp64 conv, BN and "
-                      f"SiLU passes, {t_total:.1f} s on {threads} threads"}
+def device_info() -> dict:
+    import ctypes
+    from conv_bn_silu_amd import binding as B
+    cu, clk, mclk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    rc = B.lib.conv_bn_silu_bench_device_info(ctypes.byref(cu), ctypes.byref(clk), ctypes.byref(mclk))
+    if rc:
+        return {}
+    return {"num_cu": cu.value, "peak_clock_mhz": clk.value / 1000, "mem_clock_mhz": mclk.value / 1000}
 
 
-def copy_ceiling(mib: int = 1024, reps: int = 20) -> dict:
-    """The HBM rate a plain device-to-device copy of `mib` MiB reaches on
-    this GPU (read + write bytes over the time of `reps` back-to-back
-    copies, HIP events on the copying stream): the practical ceiling for
-    the streaming layers, reported beside the 8 TB/s peak."""
+def mfma_ceiling(num_cu: int, iters: int = 20000) -> dict:
+    """Our register-only MFMA loop (k_ceiling.hip) on every compute unit:
+    the matrix-core rate this GPU sustains, beside the 2.5 PFLOP/s peak."""
     import torch
+    from conv_bn_silu_amd import binding as B
+    n_wg = 2 * num_cu  # two workgroups (eight waves) per compute unit
+    sink = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for _ in range(2):
+        assert B.lib.conv_bn_silu_bench_mfma(n_wg, iters // 10, sink.data_ptr(), sp) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    assert B.lib.conv_bn_silu_bench_mfma(n_wg, iters, sink.data_ptr(), sp) == 0
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3
+    flops = B.lib.conv_bn_silu_bench_mfma_flops(n_wg, iters)
+    return {"mfma_bf16_tflops": round(flops / sec / 1e12, 1), "mfma_seconds": round(sec, 6),
+            "mfma_what": f"v_mfma_f32_32x32x16_bf16 on registers, {n_wg} workgroups x 4 waves x {iters} x 8"}
+
+
+def copy_ceiling(num_cu: int, mib: int = 1024, reps: int = 10) -> dict:
+    """Our 16-byte streaming copy kernel (k_ceiling.hip) over `mib` MiB:
+    read + write bytes per second, the practical ceiling of the streaming
+    layers."""
+    import torch
+    from conv_bn_silu_amd import binding as B
     n = mib << 20
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     a.fill_(1)
     b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
     stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    n_wg = 8 * num_cu
+    for _ in range(2):
+        assert B.lib.conv_bn_silu_bench_copy(a.data_ptr(), b.data_ptr(), n, n_wg, sp) == 0
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(reps):
-        b.copy_(a)
+        assert B.lib.conv_bn_silu_bench_copy(a.data_ptr(), b.data_ptr(), n, n_wg, sp) == 0
     e1.record(stream)
     torch.cuda.synchronize()
     sec = e0.elapsed_time(e1) * 1e-3 / reps
     del a, b
     torch.cuda.empty_cache()
     return {"copy_gbs": round(2 * n / sec / 1e9, 1), "copy_bytes_each_way": n,
-            "what": "torch device-to-device copy, read + write bytes per second"}
+            "copy_what": f"16-byte load/store copy kernel, {n_wg} workgroups of 256"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_passes(key: str, min_seconds: float, max_reps: int = 50) -> dict:
+    """The oracle as it stands (conv, BN and SiLU passes, fp64) on one
+    workload, each pass timed on its own, repeated until ~min_seconds."""
+    import oracle
+    from conv_bn_silu_amd import synth
+    wl = synth.WORKLOADS[key]
+    inp = synth.make_inputs(wl)
+    o = oracle.get()
+    per = {"conv": 0.0, "bn": 0.0, "silu": 0.0}
+    reps = 0
+    while reps < max_reps and (reps == 0 or sum(per.values()) < min_seconds):
+        t0 = time.perf_counter()
+        t1 = o.conv(inp.x, inp.w, wl.stride, wl.pad)
+        t_a = time.perf_counter()
+        t2 = o.bn(t1, inp.scale, inp.bias)
+        t_b = time.perf_counter()
+        o.silu(t2)
+        t_c = time.perf_counter()
+        per["conv"] += t_a - t0
+        per["bn"] += t_b - t_a
+        per["silu"] += t_c - t_b
+        reps += 1
+    total = sum(per.values()) / reps
+    return {"workload": wl.name, "reps": reps, "seconds_per_pass": {k: round(v / reps, 4) for k, v in per.items()},
+            "seconds_per_call": round(total, 4), "fp64_gflops": round(wl.flops / total / 1e9, 3)}
+
+
+def cpu_baseline(key: str, gpu_tflops: float, min_seconds: float = 10.0) -> dict:
+    """The oracle on the host cores: the headline workload on every thread
+    OpenMP uses, then c1, c2 and c4 on one thread (in a child process with
+    OMP_NUM_THREADS=1), each pass timed on its own."""
+    from conv_bn_silu_amd import synth
+    wl = synth.WORKLOADS[key]
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    mt = oracle_passes(key, min_seconds)
+    code = ("import json, sys; sys.path.insert(0, %r); import bench; "
+            "print(json.dumps({k: bench.oracle_passes(k, 0.0, 1) for k in ('c1', 'c2', 'c4')}))" % ROOT)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    single = None
+    try:
+        res = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=300)
+        if res.returncode == 0:
+            single = json.loads(res.stdout.strip().splitlines()[-1])
+    except (subprocess.TimeoutExpired, ValueError, IndexError):
+        single = None
+    value = wl.flops / mt["seconds_per_call"] / 1e12
+    return {"value": round(value, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole workload {wl.name} ({wl.flops / 1e9:.1f} GFLOP) x{mt['reps']}: fp64 conv, BN "
+                      f"and SiLU passes, each timed, on {threads} threads",
+            "cpu_model": cpu_model(), "seconds_per_pass": mt["seconds_per_pass"],
+            "fp64_gflops": mt["fp64_gflops"], "gpu_over_oracle": round(gpu_tflops / value, 1),
+            "single_thread": single}
 
 
 def copy_calibration(mib: int, reps: int) -> None:
@@ -278,17 +355,76 @@ def copy_calibration(mib: int, reps: int) -> None:
     print(json.dumps({"copy_bytes": n, "reps": reps}), flush=True)
 
 
+def layer_entry(q: dict, ceil: dict) -> dict:
+    wl = q["wl"]
+    peak = MFMA_F32_TFLOPS if wl.dtype == 0 else MFMA_BF16_TFLOPS
+    ent = {"variant": q["variant"], "kernel_us": round(q["kernel_s"] * 1e6, 3),
+           "wall_us_per_step": round(q["wall_per_step_s"] * 1e6, 3),
+           "tflops": round(q["tflops_kernel"], 3), "hbm_gbs_algorithmic": round(q["hbm_gbs_alg"], 1),
+           "bound": q["roofline"]["bound"], "frac": q["roofline"]["frac"],
+           "mfma_frac": round(q["tflops_kernel"] / peak, 4),
+           "hbm_frac": round(q["hbm_gbs_alg"] / HBM_PEAK_GBS, 4),
+           "flops": wl.flops, "algorithmic_bytes": wl.algorithmic_bytes}
+    if "copy_gbs" in ceil:
+        ent["frac_of_copy_ceiling"] = round(q["hbm_gbs_alg"] / ceil["copy_gbs"], 4)
+    if "mfma_bf16_tflops" in ceil and wl.dtype == 1:
+        ent["frac_of_mfma_ceiling"] = round(q["tflops_kernel"] / ceil["mfma_bf16_tflops"], 4)
+    tr = traffic_for(wl, q["variant"])
+    if tr:
+        ent["traffic_bytes"] = tr["traffic_bytes_per_launch"]
+        ent["traffic_over_algorithmic"] = tr["traffic_over_algorithmic"]
+    return ent
+
+
+# Shapes on both sides of each dispatch rule (N, C_in, H, W, C_out, KH, KW,
+# stride, pad, dtype): the scalar kernel's size limit, the 1x1 kernel's
+# channel limit, the strided-row kernel's channel range, the 32x32 window
+# kernel's channel threshold and tile-fill threshold.
+DISPATCH_SWEEP = [
+    (1, 16, 32, 32, 32, 3, 3, 1, 1, 0), (1, 16, 48, 48, 32, 3, 3, 1, 1, 0), (1, 16, 64, 64, 32, 3, 3, 1, 1, 0),
+    (1, 16, 32, 32, 32, 3, 3, 1, 1, 1), (1, 16, 48, 48, 32, 3, 3, 1, 1, 1), (1, 32, 64, 64, 64, 3, 3, 1, 1, 1),
+    (8, 256, 40, 40, 256, 1, 1, 1, 0, 1), (8, 512, 40, 40, 256, 1, 1, 1, 0, 1), (8, 64, 80, 80, 128, 1, 1, 1, 0, 1),
+    (16, 32, 160, 160, 64, 3, 3, 2, 1, 1), (16, 64, 160, 160, 128, 3, 3, 2, 1, 1),
+    (16, 96, 80, 80, 192, 3, 3, 2, 1, 1), (16, 128, 80, 80, 256, 3, 3, 2, 1, 1),
+    (32, 64, 20, 20, 256, 3, 3, 1, 1, 1), (32, 96, 20, 20, 256, 3, 3, 1, 1, 1),
+    (32, 128, 20, 20, 256, 3, 3, 1, 1, 1), (32, 256, 20, 20, 256, 3, 3, 1, 1, 1),
+    (32, 256, 16, 16, 256, 3, 3, 1, 1, 1), (32, 256, 24, 24, 256, 3, 3, 1, 1, 1),
+    (32, 256, 40, 40, 256, 3, 3, 1, 1, 1), (16, 256, 10, 10, 512, 3, 3, 1, 1, 1),
+]
+
+
+def dispatch_check(wl, steps: int, warmup: int) -> dict:
+    """Every variant that supports the shape, timed; AUTO's pick against the
+    fastest."""
+    from conv_bn_silu_amd import binding as B
+    L = Layer(wl)
+    times = {}
+    macs = wl.flops // 2
+    for name, v in B.VARIANTS.items():
+        if v == 0 or not B.variant_supports(v, *L.geo):
+            continue
+        if name == "scalar" and macs > (1 << 31):
+            continue  # a minute of scalar work per call; never the fastest there
+        n_st = steps if name != "scalar" else max(3, steps // 10)
+        times[name] = round(measure_fused(wl, n_st, min(warmup, 3), name, L)["kernel_s"] * 1e6, 3)
+    picked = B.variant_name(B.select_variant(*L.geo))
+    fastest = min(times, key=times.get)
+    del L
+    return {"variants_us": times, "auto_picks": picked, "fastest": fastest,
+            "auto_over_fastest": round(times[picked] / times[fastest], 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", help="c1..c5 (default c2, the bf16 1x1 layer)")
+    ap.add_argument("--workload", default=HEADLINE, help="headline layer, c1..c5 (default c5)")
     ap.add_argument("--variant", default="auto")
-    ap.add_argument("--layers", action="store_true", help="also measure all five layers")
-    ap.add_argument("--unfused", action="store_true", help="also time the three-kernel sequence per layer")
-    ap.add_argument("--variants", action="store_true", help="also time every supporting variant per layer")
+    ap.add_argument("--only", action="store_true", help="only the headline layer (profiling runs)")
+    ap.add_argument("--variants", action="store_true", help="also check the dispatch on a shape sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -306,82 +442,79 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, max(1, args.steps))
         return
-    from conv_bn_silu_amd import binding as B, synth
+    from conv_bn_silu_amd import synth
+    wl = synth.WORKLOADS[args.workload]
+    dev = device_info()
+    num_cu = dev.get("num_cu", 256)
+    ceil = {}
+    if not args.only:
+        ceil.update(copy_ceiling(num_cu))
+        ceil.update(mfma_ceiling(num_cu))
+        log(f"[bench] ceilings: copy {ceil['copy_gbs']:.0f} GB/s, MFMA {ceil['mfma_bf16_tflops']:.0f} TFLOP/s")
+
     log(f"[bench] {args.workload} variant {args.variant}: {args.warmup} warmup + {args.steps} steps")
-    r = measure_fused(args.workload, args.steps, args.warmup, args.variant)
-    wl = r["wl"]
-    log(f"[bench] {wl.name}: {r['kernel_us_mean']:.2f} us/launch ({r['variant']})")
+    r = measure_fused(wl, args.steps, args.warmup, args.variant)
+    log(f"[bench] {wl.name}: {r['kernel_s'] * 1e6:.2f} us/launch ({r['variant']}), "
+        f"{r['wall_per_step_s'] * 1e6:.2f} us/step wall")
     roof = dict(r["roofline"])
-    roof["traffic"] = traffic_for(wl)
+    tr = traffic_for(wl, r["variant"])
+    roof["traffic"] = tr["traffic_bytes_per_launch"] if tr else None
     out = {
         "metric": METRIC,
-        "value": round(r["tflops"], 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == synth.DTYPE_BF16 else "f32",
+        "value": round(r["tflops_wall"], 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["wall_per_step_s"] * 1e3, 5), "higher_is_better": True,
+        "scaling": None, "vs_baseline": None, "dtype": "bf16" if wl.dtype == synth.DTYPE_BF16 else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "N": wl.N, "C_in": wl.C_in, "H": wl.H, "W": wl.W, "C_out": wl.C_out,
                    "KH": wl.KH, "KW": wl.KW, "stride": wl.stride, "pad": wl.pad, "variant": r["variant"],
-                   "rotated_buffer_sets": r["sets"], "kernel_us_mean": round(r["kernel_us_mean"], 3),
+                   "rotated_buffer_sets": r["sets"], "kernel_us_mean": round(r["kernel_s"] * 1e6, 3),
                    "host_issue_us_per_step": round(r["host_issue_us_per_step"], 3),
-                   "launch_events_us_mean": round(r["launch_events_us_mean"], 3),
-                   "launch_events_us_median": round(r["launch_events_us_median"], 3),
-                   "algorithmic_bytes": wl.algorithmic_bytes, "flops": wl.flops},
+                   "algorithmic_bytes": wl.algorithmic_bytes, "flops": wl.flops, **dev},
         "roofline": roof,
     }
-    ceil = copy_ceiling()
-    log(f"[bench] copy ceiling: {ceil['copy_gbs']:.0f} GB/s")
-    out["ceilings"] = ceil
-    sub_steps = max(20, args.steps // 2)
-    if args.layers or args.unfused or args.variants:
+    if not args.only:
+        out["ceilings"] = ceil
+        out["roofline"]["frac_of_measured_ceiling"] = round(
+            r["tflops_kernel"] / ceil["mfma_bf16_tflops"] if roof["bound"] == "mfma"
+            else r["hbm_gbs_alg"] / ceil["copy_gbs"], 4)
+        sub_steps = max(20, args.steps // 2)
         layers = {}
         for key in sorted(synth.WORKLOADS):
-            q = r if key == args.workload and args.variant == "auto" else None
-            if args.layers or args.unfused:
-                q = q or measure_fused(key, sub_steps, args.warmup)
-            ent = {}
-            if q is not None:
-                ent = {"variant": q["variant"], "kernel_us": round(q["kernel_us_mean"], 3),
-                       "tflops": round(q["tflops_kernel"], 3),
-                       "hbm_gbs_algorithmic": round(q["hbm_gbs_alg"], 1),
-                       "bound": q["roofline"]["bound"], "frac": q["roofline"]["frac"],
-                       "mfma_frac": round(q["tflops_kernel"] / (MFMA_F32_TFLOPS if q["wl"].dtype == 0
-                                                                 else MFMA_BF16_TFLOPS), 4),
-                       "hbm_frac": round(q["hbm_gbs_alg"] / HBM_PEAK_GBS, 4),
-                       "frac_of_copy": round(q["hbm_gbs_alg"] / ceil["copy_gbs"], 4),
-                       "kernel_us_median_launch": round(q["launch_events_us_median"], 3)}
-                log(f"[bench] layer {key}: {q['kernel_us_mean']:.2f} us ({q['variant']})")
-            if args.unfused:
-                u = measure_unfused(key, sub_steps, args.warmup)
-                ent["unfused_us_per_step"] = round(u["us_per_step"], 3)
-                ent["fused_us_per_step"] = round(q["region_us_per_step"], 3)
-                ent["fused_speedup"] = round(u["us_per_step"] / q["region_us_per_step"], 3)
-                log(f"[bench] layer {key}: unfused {u['us_per_step']:.2f} us/step")
-            if args.variants:
-                wlk = synth.WORKLOADS[key]
-                geo = (wlk.N, wlk.C_in, wlk.H, wlk.W, wlk.C_out, wlk.KH, wlk.KW, wlk.stride, wlk.pad, wlk.dtype)
-                L = Layer(key)
-                times = {}
-                for name, v in B.VARIANTS.items():
-                    if v == 0 or not B.variant_supports(v, *geo):
-                        continue
-                    # the scalar variant is very slow on the large layers: fewer steps
-                    n_st = sub_steps if name != "scalar" else 5
-                    times[name] = round(measure_fused(key, n_st, min(args.warmup, 3), name, L)
-                                        ["kernel_us_mean"], 3)
-                    log(f"[bench] layer {key} variant {name}: {times[name]:.2f} us")
-                picked = B.variant_name(B.select_variant(*geo))
-                ent["variants_us"] = times
-                ent["auto_picks"] = picked
-                ent["auto_is_fastest"] = picked == min(times, key=times.get)
-                del L
-            layers[synth.WORKLOADS[key].name] = ent
+            wlk = synth.WORKLOADS[key]
+            q = r if key == args.workload and args.variant == "auto" else measure_fused(wlk, sub_steps, args.warmup)
+            ent = layer_entry(q, ceil)
+            u = measure_unfused(wlk, sub_steps, args.warmup)
+            ent["unfused_us_per_step"] = round(u["us_per_step"], 3)
+            ent["fused_speedup_over_unfused"] = round(u["us_per_step"] / (q["kernel_s"] * 1e6), 3)
+            log(f"[bench] layer {key}: {ent['kernel_us']:.2f} us ({ent['variant']}, frac {ent['frac']}), "
+                f"unfused {ent['unfused_us_per_step']:.2f} us")
+            layers[wlk.name] = ent
         out["layers"] = layers
-    if args.no_cpu_baseline:
+    if args.variants:
+        checks = []
+        shapes = [(k, synth.WORKLOADS[k]) for k in sorted(synth.WORKLOADS)]
+        for i, g in enumerate(DISPATCH_SWEEP):
+            seed = 7000 + i
+            shapes.append((f"sweep{i}", synth.Workload(f"sweep{i}", g[9], *g[:9], "n01", seed)))
+        for key, wlk in shapes:
+            c = dispatch_check(wlk, max(10, args.steps // 10), args.warmup)
+            c["shape"] = [wlk.N, wlk.C_in, wlk.H, wlk.W, wlk.C_out, wlk.KH, wlk.KW, wlk.stride, wlk.pad, wlk.dtype]
+            c["name"] = wlk.name
+            log(f"[bench] dispatch {wlk.name}: auto {c['auto_picks']}, fastest {c['fastest']}, "
+                f"ratio {c['auto_over_fastest']}")
+            checks.append(c)
+        worst = max(c["auto_over_fastest"] for c in checks)
+        out["dispatch"] = {"shapes": checks, "worst_auto_over_fastest": worst,
+                           "auto_within_5pct": worst <= DISPATCH_SLACK}
+    if args.no_cpu_baseline or args.only:
         out["cpu_baseline"] = None
     else:
         log("[bench] cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(args.workload)
+        out["cpu_baseline"] = cpu_baseline(args.workload, r["tflops_kernel"], args.cpu_seconds)
     print(json.dumps(out), flush=True)
+    if args.variants and not out["dispatch"]["auto_within_5pct"]:
+        log(f"[bench] dispatch check failed: AUTO is {out['dispatch']['worst_auto_over_fastest']}x the fastest")
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -3,17 +3,18 @@
 profiles/ (run on a machine with the GPU; raw profiler output stays in
 gpurun_out/).
 
-  python3 bench_profile.py trace   [--workload c2]
-      rocprofv3 --kernel-trace --stats over the default bench command (or the
-      named workload); writes profiles/kernel_trace_<workload>.md with the
-      per-kernel durations and the bench's own JSON line from the same run.
+  python3 bench_profile.py trace   [--workload c5]
+      rocprofv3 --kernel-trace --stats over the bench command for the named
+      workload alone (bench.py --only); writes
+      profiles/kernel_trace_<workload>.md with the per-kernel durations and
+      the bench's own JSON line from the same run.
 
-  python3 bench_profile.py traffic [--workload c2]
+  python3 bench_profile.py traffic [--workload c5]
       four counter runs, each on its own: FETCH_SIZE and WRITE_SIZE over a
       plain 1 GiB device copy (to scale the counters to bytes), then
       FETCH_SIZE and WRITE_SIZE over the bench command; writes
       profiles/traffic_<workload>.md, which bench.py reads back while the
-      kernel sources are unchanged.
+      source of the variant's kernel is unchanged.
 
   python3 bench_profile.py mfma    [--workload c5]
       one counter run (SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16)
@@ -21,6 +22,10 @@ gpurun_out/).
       profiles/mfma_<workload>.md with the matrix-core busy fraction of the
       operator's kernel and the MFMA work it counted against the layer's
       algorithmic FLOP.
+
+  python3 bench_profile.py all
+      trace for c1..c5, traffic for c2..c5, mfma for c5: each rocprofv3 pass
+      a run of its own.
 
 This process never touches the GPU itself: rocprofv3 starts bench.py as a
 child.
@@ -69,9 +74,7 @@ def last_json(text: str) -> dict:
 
 
 def bench_cmd(workload: str, steps: int | None = None, extra: tuple = ()) -> list[str]:
-    cmd = ["python3", "bench.py"]
-    if workload != "c2":
-        cmd += ["--workload", workload]
+    cmd = ["python3", "bench.py", "--only", "--workload", workload]
     if steps is not None:
         cmd += ["--steps", str(steps), "--warmup", "2"]
     return cmd + list(extra)
@@ -89,7 +92,7 @@ def workload_name(key: str) -> str:
 
 def do_trace(args) -> None:
     out = os.path.join(RAW, f"trace_{args.workload}")
-    cmd = bench_cmd(args.workload)
+    cmd = bench_cmd(args.workload, 100)
     prof = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", out, "-o", "run", "--"]
     stdout = run(prof + cmd, 400)
     line = last_json(stdout)
@@ -107,7 +110,8 @@ def do_trace(args) -> None:
             "Kernels by total time (durations in microseconds):", "",
             "| kernel | calls | avg | min | max | % time |", "|---|---|---|---|---|---|"] + rows + [
             "", "bench.py's own JSON line from the same run (kernel_us_mean: HIP events around the timed "
-            "region on the launch stream, per launch):", "", "```json", json.dumps(line), "```", ""]
+            "region on the launch stream, per launch; the average above also counts the warm-up "
+            "launches):", "", "```json", json.dumps(line), "```", ""]
     os.makedirs(args.out, exist_ok=True)
     path = os.path.join(args.out, f"kernel_trace_{name}.md")
     with open(path, "w") as f:
@@ -154,11 +158,12 @@ def do_traffic(args) -> None:
                                   "factor": (copy_mib << 20) / (kib * 1024.0)}
         cmds[f"copy_{counter}"] = " ".join(["timeout -s KILL 60"] + c).replace(out, "gpurun_out/rocprof/copy")
     dominant = None
+    variant = None
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         out = os.path.join(RAW, f"{args.workload}_{counter.lower()}")
         c = ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", out, "-o", "run", "--"] + \
-            bench_cmd(args.workload, 20, ("--no-cpu-baseline",))
-        run(c, 60)
+            bench_cmd(args.workload, 20)
+        variant = last_json(run(c, 60))["config"]["variant"]
         by = counter_by_kernel(os.path.join(out, "run_counter_collection.csv"), counter, lambda k: "cbs" in k)
         if dominant is None:  # the operator's kernel that fetches the most
             dominant = max(by, key=lambda n: sum(by[n]))
@@ -170,7 +175,7 @@ def do_traffic(args) -> None:
     wl = synth.WORKLOADS[args.workload]
     fetch = res["FETCH_SIZE"]["kib_per_dispatch"] * 1024 * res["copy_FETCH_SIZE"]["factor"]
     write = res["WRITE_SIZE"]["kib_per_dispatch"] * 1024 * res["copy_WRITE_SIZE"]["factor"]
-    rec = {"workload": wl.name, "kernel": res["FETCH_SIZE"]["kernel"],
+    rec = {"workload": wl.name, "variant": variant, "kernel": res["FETCH_SIZE"]["kernel"],
            "fetch_kib_per_dispatch_raw": round(res["FETCH_SIZE"]["kib_per_dispatch"], 1),
            "write_kib_per_dispatch_raw": round(res["WRITE_SIZE"]["kib_per_dispatch"], 1),
            "copy_bytes": copy_mib << 20,
@@ -181,7 +186,7 @@ def do_traffic(args) -> None:
            "algorithmic_bytes": wl.algorithmic_bytes,
            "other_kernels_fetch_kib_raw": res["FETCH_SIZE"]["other_kernels_kib"],
            "traffic_over_algorithmic": round((fetch + write) / wl.algorithmic_bytes, 4),
-           "kernel_sources_digest": bench.kernel_sources_digest()}
+           "kernel_sources_digest": bench.kernel_sources_digest(variant)}
     text = [f"# HBM traffic: fused conv+BN+SiLU, workload {wl.name}", "",
             "Each counter in a run of its own (from the repository root, on one MI355X):", "",
             "```"] + [cmds[k] for k in ("copy_FETCH_SIZE", "copy_WRITE_SIZE", "FETCH_SIZE", "WRITE_SIZE")] + [
@@ -201,8 +206,8 @@ def do_mfma(args) -> None:
     counters = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16"]
     out = os.path.join(RAW, f"{args.workload}_mfma")
     c = ["rocprofv3", "--pmc"] + counters + ["--output-format", "csv", "-d", out, "-o", "run", "--"] + \
-        bench_cmd(args.workload, 20, ("--no-cpu-baseline",))
-    run(c, 60)
+        bench_cmd(args.workload, 20)
+    variant = last_json(run(c, 60))["config"]["variant"]
     path = os.path.join(out, "run_counter_collection.csv")
     vals = {}
     for ctr in counters:
@@ -219,13 +224,13 @@ def do_mfma(args) -> None:
     wl = synth.WORKLOADS[args.workload]
     simds, clock = 4 * 256, 2.4e9
     busy, mops = vals[counters[0]][1], vals[counters[1]][1]
-    rec = {"workload": wl.name, "kernel": kname[:100], "dispatches": vals[counters[0]][2],
+    rec = {"workload": wl.name, "variant": variant, "kernel": kname[:100], "dispatches": vals[counters[0]][2],
            "SQ_VALU_MFMA_BUSY_CYCLES": busy, "SQ_INSTS_VALU_MFMA_MOPS_BF16": mops,
            "mfma_busy_cycles_per_simd": round(busy / simds), "dispatch_duration_us": round(dur * 1e6, 3),
            "mfma_busy_pct": round(100.0 * busy / simds / (dur * clock), 2),
            "mfma_flop_counted": mops * 512, "algorithmic_flop": wl.flops,
            "counted_over_algorithmic": round(mops * 512 / wl.flops, 4),
-           "kernel_sources_digest": __import__("bench").kernel_sources_digest()}
+           "kernel_sources_digest": __import__("bench").kernel_sources_digest(variant)}
     text = [f"# Matrix-core use: fused conv+BN+SiLU, workload {wl.name}", "",
             "Counter run (from the repository root, on one MI355X):", "", "```",
             " ".join(["timeout -s KILL 60"] + c).replace(out, f"gpurun_out/rocprof/{args.workload}_mfma"), "```", "",
@@ -245,19 +250,26 @@ def do_mfma(args) -> None:
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("mode", choices=["trace", "traffic", "mfma"])
-    ap.add_argument("--workload", default="c2")
+    ap.add_argument("mode", choices=["trace", "traffic", "mfma", "all"])
+    ap.add_argument("--workload", default="c5")
     ap.add_argument("--out", default=PROFILES, help="where the summaries go (default profiles/)")
     args = ap.parse_args()
     os.makedirs(RAW, exist_ok=True)
     if args.mode == "trace":
         do_trace(args)
     elif args.mode == "mfma":
-        if args.workload == "c2" and "--workload" not in sys.argv:
-            args.workload = "c5"
         do_mfma(args)
-    else:
+    elif args.mode == "traffic":
         do_traffic(args)
+    else:
+        for key in ("c1", "c2", "c3", "c4", "c5"):
+            args.workload = key
+            do_trace(args)
+        for key in ("c2", "c3", "c4", "c5"):
+            args.workload = key
+            do_traffic(args)
+        args.workload = "c5"
+        do_mfma(args)
 
 
 if __name__ == "__main__":

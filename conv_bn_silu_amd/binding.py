@@ -25,12 +25,18 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 VARIANTS = {"auto": 0, "gemm_gather": 1, "gemm_window": 2, "pointwise": 3, "small_k": 4, "scalar": 5,
             "gemm_window32": 6, "strided_rows": 7}
 
-# Every symbol the header declares; the CPU tests check the library exports each.
+# Every symbol include/conv_bn_silu.h declares; the CPU tests check the
+# library exports each.
 EXPORTS = [
     "conv_bn_silu_create", "conv_bn_silu_destroy", "conv_bn_silu_run", "conv_bn_silu_run_variant",
     "conv_bn_silu_run_unfused", "conv_bn_silu_output_hw", "conv_bn_silu_validate",
     "conv_bn_silu_select_variant", "conv_bn_silu_variant_supports", "conv_bn_silu_status_string",
     "conv_bn_silu_variant_name", "conv_bn_silu_last_hip_error", "conv_bn_silu_fold_bn",
+]
+# Measurement support (include/conv_bn_silu_bench.h).
+BENCH_EXPORTS = [
+    "conv_bn_silu_bench_device_info", "conv_bn_silu_bench_mfma", "conv_bn_silu_bench_mfma_flops",
+    "conv_bn_silu_bench_copy",
 ]
 
 
@@ -69,6 +75,14 @@ def _load() -> ctypes.CDLL:
     for name in EXPORTS:
         if name not in ("conv_bn_silu_status_string", "conv_bn_silu_variant_name"):
             getattr(lib, name).restype = i
+    lib.conv_bn_silu_bench_device_info.argtypes = [ip, ip, ip]
+    lib.conv_bn_silu_bench_device_info.restype = i
+    lib.conv_bn_silu_bench_mfma.argtypes = [i, i, vp, vp]
+    lib.conv_bn_silu_bench_mfma.restype = i
+    lib.conv_bn_silu_bench_mfma_flops.argtypes = [i, i]
+    lib.conv_bn_silu_bench_mfma_flops.restype = ctypes.c_int64
+    lib.conv_bn_silu_bench_copy.argtypes = [vp, vp, ctypes.c_uint64, i, vp]
+    lib.conv_bn_silu_bench_copy.restype = i
     return lib
 
 
@@ -122,7 +136,9 @@ def fold_bn(gamma, beta, mean, var, eps, conv_bias=None):
 
 
 class Library:
-    """One handle on the current device (conv_bn_silu_create/destroy)."""
+    """One handle on the current device (conv_bn_silu_create/destroy).  The
+    handle is read-only after creation: one may serve every stream and
+    thread of the process."""
 
     def __init__(self):
         h = ctypes.c_void_p()
@@ -178,6 +194,8 @@ def _geometry(x, w, scale, bias, stride, pad):
     for t in (x, w, scale, bias):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("all tensors must be contiguous device tensors")
+        if t.device != x.device:
+            raise ValueError("all tensors must be on x's device")
     N, C_in, H, W = x.shape
     C_out, C_in_w, KH, KW = w.shape
     if C_in_w != C_in or scale.numel() != C_out or bias.numel() != C_out:
@@ -185,6 +203,15 @@ def _geometry(x, w, scale, bias, stride, pad):
     OH, OW = output_hw(H, W, KH, KW, stride, pad)
     dtype = DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_F32
     return (N, C_in, H, W, C_out, KH, KW, stride, pad, dtype), (N, C_out, OH, OW)
+
+
+def _check_output(t, x, yshape, what):
+    """An output buffer the kernels may write: x's device, dtype, the output
+    shape, contiguous."""
+    if not t.is_cuda or t.device != x.device:
+        raise ValueError(f"{what} must be a device tensor on x's device")
+    if tuple(t.shape) != yshape or t.dtype != x.dtype or not t.is_contiguous():
+        raise ValueError(f"{what} has the wrong shape, dtype or layout")
 
 
 def conv_bn_silu(x, w, scale, bias, stride: int = 1, pad: int = 0, out=None, variant: str = "auto",
@@ -197,8 +224,7 @@ def conv_bn_silu(x, w, scale, bias, stride: int = 1, pad: int = 0, out=None, var
     import torch
     geo, yshape = _geometry(x, w, scale, bias, stride, pad)
     y = torch.empty(yshape, dtype=x.dtype, device=x.device) if out is None else out
-    if tuple(y.shape) != yshape or y.dtype != x.dtype or not y.is_contiguous():
-        raise ValueError("out has the wrong shape, dtype or layout")
+    _check_output(y, x, yshape, "out")
     lib_ = library or default_library()
     stream = torch.cuda.current_stream(x.device).cuda_stream
     lib_.run_ptr(VARIANTS[variant], x.data_ptr(), w.data_ptr(), scale.data_ptr(), bias.data_ptr(),
@@ -206,12 +232,19 @@ def conv_bn_silu(x, w, scale, bias, stride: int = 1, pad: int = 0, out=None, var
     return y
 
 
-def conv_bn_silu_unfused(x, w, scale, bias, stride: int = 1, pad: int = 0, library: Library | None = None):
+def conv_bn_silu_unfused(x, w, scale, bias, stride: int = 1, pad: int = 0, library: Library | None = None,
+                         out=None):
     """The three-kernel sequence conv -> BN -> SiLU with t1, t2 in memory;
-    returns (y, t1, t2)."""
+    returns (y, t1, t2).  `out`, if given, is a tuple (y, t1, t2) of buffers
+    to write."""
     import torch
     geo, yshape = _geometry(x, w, scale, bias, stride, pad)
-    t1, t2, y = (torch.empty(yshape, dtype=x.dtype, device=x.device) for _ in range(3))
+    if out is None:
+        y, t1, t2 = (torch.empty(yshape, dtype=x.dtype, device=x.device) for _ in range(3))
+    else:
+        y, t1, t2 = out
+        for t, name in ((y, "y"), (t1, "t1"), (t2, "t2")):
+            _check_output(t, x, yshape, name)
     lib_ = library or default_library()
     stream = torch.cuda.current_stream(x.device).cuda_stream
     lib_.run_unfused_ptr(x.data_ptr(), w.data_ptr(), scale.data_ptr(), bias.data_ptr(), t1.data_ptr(),

@@ -1,11 +1,11 @@
 // cbs_api.cpp -- the C ABI declared in include/conv_bn_silu.h: handles,
 // host-side validation, variant dispatch and kernel launch.
 //
-// Nothing here touches device memory; every argument is checked before the
-// first HIP call, and every failure is reported as a status code.
+// Nothing here touches device memory and nothing allocates it: every
+// argument is checked before the first HIP call, every failure is reported as
+// a status code, and a run call only enqueues kernels on the caller's stream.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -17,20 +17,20 @@
 #include "cbs_shape.h"
 
 struct conv_bn_silu_handle {
+    // Fixed at create and only read afterwards, so one handle may serve
+    // concurrent calls from any number of threads and streams.
     int device;
     int num_cu;
-    std::atomic<int> last_hip_error;
-    // Device workspace for packed weights, grown on demand and kept until
-    // the handle is destroyed.
-    std::mutex ws_mu;
-    void *ws = nullptr;
-    size_t ws_bytes = 0;
 };
 
 namespace {
 
 std::mutex g_handles_mu;
 std::set<const conv_bn_silu_handle *> g_handles;  // live handles; never dereference a foreign pointer
+
+// The hipError_t of the last failed HIP call this thread made through the
+// library (kept per thread, so that handles stay read-only).
+thread_local int t_last_hip_error = 0;
 
 bool handle_live(const conv_bn_silu_handle *h) {
     std::lock_guard<std::mutex> lk(g_handles_mu);
@@ -76,14 +76,16 @@ int check_pointers(const void *x, const void *w, const float *scale, const float
                    const cbs::Shape &s, int dtype) {
     if (!x || !w || !scale || !bias || !y) return CBS_ERR_INVALID_ARG;
     const uintptr_t e = dtype == CBS_DTYPE_BF16 ? 2 : 4;
-    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) % e != 0) return CBS_ERR_INVALID_ARG;
-    if (((uintptr_t)scale | (uintptr_t)bias) % 4 != 0) return CBS_ERR_INVALID_ARG;
     const Range rx{(uintptr_t)x, (uintptr_t)x + (uintptr_t)s.N * s.C_in * s.HW * e};
     const Range rw{(uintptr_t)w, (uintptr_t)w + (uintptr_t)s.C_out * s.K * e};
     const Range rs{(uintptr_t)scale, (uintptr_t)scale + (uintptr_t)s.C_out * 4};
     const Range rb{(uintptr_t)bias, (uintptr_t)bias + (uintptr_t)s.C_out * 4};
     const Range ry{(uintptr_t)y, (uintptr_t)y + (uintptr_t)s.N * s.C_out * s.OHW * e};
     if (overlap(ry, rx) || overlap(ry, rw) || overlap(ry, rs) || overlap(ry, rb)) return CBS_ERR_INVALID_ARG;
+    // Pointers off their element size are well-formed requests the kernels
+    // do not serve.
+    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) % e != 0) return CBS_ERR_UNSUPPORTED;
+    if (((uintptr_t)scale | (uintptr_t)bias) % 4 != 0) return CBS_ERR_UNSUPPORTED;
     return CBS_OK;
 }
 
@@ -115,6 +117,8 @@ bool pointers_ok(int variant, const void *x, const void *w, const void *y) {
         case CBS_VARIANT_POINTWISE: return cbs::pointwise_pointers_ok(x, w, y);
         case CBS_VARIANT_SMALL_K: return cbs::stem_pointers_ok(x, w, y);
         case CBS_VARIANT_ROWS: return cbs::rows_pointers_ok(x, w, y);
+        case CBS_VARIANT_GEMM_WINDOW: return cbs::window_pointers_ok(x, w, y);
+        case CBS_VARIANT_GEMM_WINDOW32: return cbs::window32_pointers_ok(x, w, y);
         default: return true;
     }
 }
@@ -144,28 +148,8 @@ int select_for_call(const cbs::Shape &s, int dtype, int num_cu, const void *x, c
     return pointers_ok(v, x, w, y) ? v : CBS_VARIANT_GEMM_GATHER;
 }
 
-// Make the handle's workspace at least `bytes` long.  Growing it frees the
-// old buffer (which waits for the device) and allocates a new one.
-hipError_t ensure_workspace(conv_bn_silu_handle *h, size_t bytes, void **out) {
-    std::lock_guard<std::mutex> lk(h->ws_mu);
-    if (h->ws_bytes < bytes) {
-        if (h->ws) {
-            (void)hipFree(h->ws);
-            h->ws = nullptr;
-            h->ws_bytes = 0;
-        }
-        const size_t want = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
-        const hipError_t e = hipMalloc(&h->ws, want);
-        if (e != hipSuccess) return e;
-        h->ws_bytes = want;
-    }
-    *out = h->ws;
-    return hipSuccess;
-}
-
 hipError_t launch(int variant, const cbs::Shape &s, int dtype, int epi, const void *x, const void *w,
-                  const float *scale, const float *bias, void *y, hipStream_t st, int num_cu,
-                  void *workspace) {
+                  const float *scale, const float *bias, void *y, hipStream_t st, int num_cu) {
     // hipGetLastError reports the last error of any HIP call on this thread;
     // clear whatever an earlier, unrelated call left so that the launcher's
     // check sees only its own launch.
@@ -174,9 +158,9 @@ hipError_t launch(int variant, const cbs::Shape &s, int dtype, int epi, const vo
         case CBS_VARIANT_GEMM_GATHER: return cbs::launch_gemm_gather(s, dtype, epi, x, w, scale, bias, y, st);
         case CBS_VARIANT_POINTWISE: return cbs::launch_pointwise(s, epi, x, w, scale, bias, y, st, num_cu);
         case CBS_VARIANT_GEMM_WINDOW:
-            return cbs::launch_window(s, epi, x, w, scale, bias, y, workspace, st, num_cu);
+            return cbs::launch_window(s, epi, x, w, scale, bias, y, st, num_cu);
         case CBS_VARIANT_GEMM_WINDOW32:
-            return cbs::launch_window32(s, epi, x, w, scale, bias, y, workspace, st, num_cu);
+            return cbs::launch_window32(s, epi, x, w, scale, bias, y, st, num_cu);
         case CBS_VARIANT_SMALL_K: return cbs::launch_stem(s, epi, x, w, scale, bias, y, st, num_cu);
         case CBS_VARIANT_ROWS: return cbs::launch_rows(s, epi, x, w, scale, bias, y, st, num_cu);
         case CBS_VARIANT_SCALAR: return cbs::launch_scalar(s, dtype, epi, x, w, scale, bias, y, st);
@@ -184,9 +168,9 @@ hipError_t launch(int variant, const cbs::Shape &s, int dtype, int epi, const vo
     }
 }
 
-int record_hip(conv_bn_silu_handle *h, hipError_t e) {
+int record_hip(hipError_t e) {
     if (e == hipSuccess) return CBS_OK;
-    h->last_hip_error.store((int)e);
+    t_last_hip_error = (int)e;
     return CBS_ERR_HIP;
 }
 
@@ -214,16 +198,17 @@ int conv_bn_silu_create(conv_bn_silu_t *out_handle) {
     if (hipGetDeviceCount(&count) != hipSuccess || count < 1) return CBS_ERR_NO_DEVICE;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return CBS_ERR_NO_DEVICE;
-    // The property record is over-allocated: the process's HIP runtime may be
-    // a different release than the headers this file was compiled with.
-    alignas(64) static thread_local unsigned char prop_buf[sizeof(hipDeviceProp_t) + 8192];
-    hipDeviceProp_t &prop = *reinterpret_cast<hipDeviceProp_t *>(prop_buf);
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return CBS_ERR_NO_DEVICE;
-    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return CBS_ERR_UNSUPPORTED;
+    // Scalar attributes only (no property record, whose layout depends on the
+    // runtime release).  The graphics IP version of gfx950 is 9.5.
+    int major = 0, minor = 0, num_cu = 0;
+    if (hipDeviceGetAttribute(&major, hipDeviceAttributeComputeCapabilityMajor, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&minor, hipDeviceAttributeComputeCapabilityMinor, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return CBS_ERR_NO_DEVICE;
+    if (major != 9 || minor != 5 || num_cu < 1) return CBS_ERR_UNSUPPORTED;
     auto *h = new conv_bn_silu_handle;
     h->device = dev;
-    h->num_cu = prop.multiProcessorCount;
-    h->last_hip_error.store(0);
+    h->num_cu = num_cu;
     {
         std::lock_guard<std::mutex> lk(g_handles_mu);
         g_handles.insert(h);
@@ -238,7 +223,6 @@ int conv_bn_silu_destroy(conv_bn_silu_t h) {
         std::lock_guard<std::mutex> lk(g_handles_mu);
         if (g_handles.erase(h) == 0) return CBS_ERR_BAD_HANDLE;
     }
-    if (h->ws) (void)hipFree(h->ws);
     delete h;
     return CBS_OK;
 }
@@ -253,13 +237,8 @@ int conv_bn_silu_run_variant(conv_bn_silu_t h, int variant, const void *x, const
     if (s.N == 0) return CBS_OK;
     if (variant == CBS_VARIANT_AUTO) variant = select_for_call(s, dtype, h->num_cu, x, w, y);
     else if (!variant_ok(variant, s, dtype) || !pointers_ok(variant, x, w, y)) return CBS_ERR_UNSUPPORTED;
-    void *ws = nullptr;
-    if (variant == CBS_VARIANT_GEMM_WINDOW || variant == CBS_VARIANT_GEMM_WINDOW32) {
-        rc = record_hip(h, ensure_workspace(h, cbs::window_workspace_bytes(s), &ws));
-        if (rc != CBS_OK) return rc;
-    }
-    return record_hip(h, launch(variant, s, dtype, cbs::kFused, x, w, scale, bias, y, (hipStream_t)stream,
-                                h->num_cu, ws));
+    return record_hip(launch(variant, s, dtype, cbs::kFused, x, w, scale, bias, y, (hipStream_t)stream,
+                             h->num_cu));
 }
 
 int conv_bn_silu_run(conv_bn_silu_t h, const void *x, const void *w, const float *scale, const float *bias,
@@ -277,7 +256,7 @@ int conv_bn_silu_run_unfused(conv_bn_silu_t h, const void *x, const void *w, con
     if (rc != CBS_OK) return rc;
     if (s.N == 0) return CBS_OK;
     const uintptr_t e = dtype == CBS_DTYPE_BF16 ? 2 : 4;
-    if (!t1 || !t2 || ((uintptr_t)t1 | (uintptr_t)t2) % e != 0) return CBS_ERR_INVALID_ARG;
+    if (!t1 || !t2) return CBS_ERR_INVALID_ARG;
     const uintptr_t ybytes = (uintptr_t)s.N * s.C_out * s.OHW * e;
     const Range r1{(uintptr_t)t1, (uintptr_t)t1 + ybytes}, r2{(uintptr_t)t2, (uintptr_t)t2 + ybytes};
     const Range others[] = {{(uintptr_t)x, (uintptr_t)x + (uintptr_t)s.N * s.C_in * s.HW * e},
@@ -288,20 +267,16 @@ int conv_bn_silu_run_unfused(conv_bn_silu_t h, const void *x, const void *w, con
     if (overlap(r1, r2)) return CBS_ERR_INVALID_ARG;
     for (const Range &o : others)
         if (overlap(r1, o) || overlap(r2, o)) return CBS_ERR_INVALID_ARG;
+    if (((uintptr_t)t1 | (uintptr_t)t2) % e != 0) return CBS_ERR_UNSUPPORTED;
     const hipStream_t st = (hipStream_t)stream;
     const int variant = select_for_call(s, dtype, h->num_cu, x, w, t1);
-    void *ws = nullptr;
-    if (variant == CBS_VARIANT_GEMM_WINDOW || variant == CBS_VARIANT_GEMM_WINDOW32) {
-        rc = record_hip(h, ensure_workspace(h, cbs::window_workspace_bytes(s), &ws));
-        if (rc != CBS_OK) return rc;
-    }
-    rc = record_hip(h, launch(variant, s, dtype, cbs::kConvOnly, x, w, scale, bias, t1, st, h->num_cu, ws));
+    rc = record_hip(launch(variant, s, dtype, cbs::kConvOnly, x, w, scale, bias, t1, st, h->num_cu));
     if (rc != CBS_OK) return rc;
     (void)hipGetLastError();
-    rc = record_hip(h, cbs::launch_bn_pass(s, dtype, t1, scale, bias, t2, st));
+    rc = record_hip(cbs::launch_bn_pass(s, dtype, t1, scale, bias, t2, st));
     if (rc != CBS_OK) return rc;
     (void)hipGetLastError();
-    return record_hip(h, cbs::launch_silu_pass(s, dtype, t2, y, st));
+    return record_hip(cbs::launch_silu_pass(s, dtype, t2, y, st));
 }
 
 int conv_bn_silu_output_hw(int H, int W, int KH, int KW, int stride, int pad, int *OH, int *OW) {
@@ -364,7 +339,7 @@ const char *conv_bn_silu_variant_name(int variant) {
 
 int conv_bn_silu_last_hip_error(conv_bn_silu_t h) {
     if (!handle_live(h)) return 0;
-    return h->last_hip_error.load();
+    return t_last_hip_error;
 }
 
 int conv_bn_silu_fold_bn(const float *gamma, const float *beta, const float *mean, const float *var, float eps,

@@ -18,7 +18,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Epilogue of "Fusing an Epilogue" (section "The shape of it"): the folded
-// batch norm is a multiply and an add with the output channel's parameters,
+// batch norm scales and shifts by the output channel's parameters,
 // then SiLU(v) = v * sigmoid(v), sigmoid(v) = 1 / (1 + e^-v).  e^-v is taken
 // as 2^(-v*log2 e) on the hardware exp2 unit and the quotient through the
 // hardware reciprocal (both about 1 ulp in fp32).  For v below about -88,

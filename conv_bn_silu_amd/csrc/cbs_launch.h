@@ -25,12 +25,12 @@ bool pointwise_pointers_ok(const void *x, const void *w, const void *y);
 hipError_t launch_pointwise(const Shape &s, int epi, const void *x, const void *w, const float *scale,
                             const float *bias, void *y, hipStream_t st, int num_cu);
 
-// Window-staged implicit GEMM (bf16; W, OW multiples of 4).  Needs a
-// workspace of window_workspace_bytes() for the packed weights.
+// Window-staged implicit GEMM (bf16; W, OW multiples of 4), weights
+// gathered from OIHW; x 16-byte and y 8-byte aligned.
 bool window_supports(const Shape &s, int dtype);
-size_t window_workspace_bytes(const Shape &s);
+bool window_pointers_ok(const void *x, const void *w, const void *y);
 hipError_t launch_window(const Shape &s, int epi, const void *x, const void *w, const float *scale,
-                         const float *bias, void *y, void *workspace, hipStream_t st, int num_cu);
+                         const float *bias, void *y, hipStream_t st, int num_cu);
 
 // Small-K stem: 3x3, stride 2, pad 1, C_in <= 3, C_out <= 16 (bf16; W a
 // multiple of 32, OW <= 320); x and y 16-byte aligned.
@@ -47,18 +47,16 @@ bool rows_pointers_ok(const void *x, const void *w, const void *y);
 hipError_t launch_rows(const Shape &s, int epi, const void *x, const void *w, const float *scale, const float *bias,
                        void *y, hipStream_t st, int num_cu);
 
-// Packs OIHW weights for the window kernels: wp[co][block][tap][32
-// channels] (zero past C_in), window_workspace_bytes() long.
-hipError_t launch_pack_weights(const Shape &s, const void *w, void *workspace, hipStream_t st);
-
-// Window-staged implicit GEMM on 32x32x16 MFMA with 7 x 2 accumulator tiles
-// per wave (bf16; W, OW multiples of 4); same workspace as the window kernel.
+// Window-staged 3x3 implicit GEMM on 32x32x16 MFMA, 13 or 14 accumulator
+// tiles per wave (bf16; W, OW multiples of 4, C_in a multiple of 8), weights
+// staged from OIHW; x and w 16-byte, y 8-byte aligned.
 // window32_efficiency: share (per mille) of a tile's matrix work that lands
 // on real output pixels.
 bool window32_supports(const Shape &s, int dtype);
+bool window32_pointers_ok(const void *x, const void *w, const void *y);
 int window32_efficiency(const Shape &s);
 hipError_t launch_window32(const Shape &s, int epi, const void *x, const void *w, const float *scale,
-                           const float *bias, void *y, void *workspace, hipStream_t st, int num_cu);
+                           const float *bias, void *y, hipStream_t st, int num_cu);
 
 // One output element per lane; any geometry, both dtypes.
 bool scalar_supports(const Shape &s, int dtype);

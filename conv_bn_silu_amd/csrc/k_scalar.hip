@@ -1,4 +1,4 @@
-// k_scalar.hip -- the scalar variant ("one output element per lane", page
+// k_scalar.hip -- the scalar variant (each lane computes one output, page
 // "Fusing an Epilogue", section "Three kernels for one operation"), and the
 // element-wise batch-norm and SiLU passes of the unfused sequence the fused
 // operator replaces (same page, section "The problem").
@@ -16,13 +16,22 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Grid-stride loop indices.  The stride (grid x 256) is added in 64 bits and
+// the loop ends once the sum passes `total`, so an index never wraps past
+// 2^31 - 1 for any total up to INT32_MAX.
+__device__ __forceinline__ int first_index() { return (int)(blockIdx.x * kThreads + threadIdx.x); }
+__device__ __forceinline__ int next_index(int idx, int total) {
+    const long long nxt = (long long)idx + (long long)gridDim.x * kThreads;
+    return nxt < total ? (int)nxt : total;
+}
+
 template <typename T, int EPI>
 __global__ __launch_bounds__(kThreads) void conv_scalar(const T *__restrict__ x, const T *__restrict__ w,
                                                         const float *__restrict__ scale,
                                                         const float *__restrict__ bias, T *__restrict__ y,
                                                         Shape s) {
     const int total = s.N * s.C_out * s.OHW;
-    for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
+    for (int idx = first_index(); idx < total; idx = next_index(idx, total)) {
         const int ow = idx % s.OW;
         const int oh = (idx / s.OW) % s.OH;
         const int co = (idx / s.OHW) % s.C_out;
@@ -58,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void conv_scalar3x3(const T *__restrict__
                                                            const float *__restrict__ bias, T *__restrict__ y,
                                                            Shape s) {
     const int total = s.N * s.C_out * s.OHW;
-    for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
+    for (int idx = first_index(); idx < total; idx = next_index(idx, total)) {
         const int ow = idx % s.OW;
         const int oh = (idx / s.OW) % s.OH;
         const int co = (idx / s.OHW) % s.C_out;
@@ -93,7 +102,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void bn_pass(const T *__restrict__ t1, const float *__restrict__ scale,
                                                     const float *__restrict__ bias, T *__restrict__ t2,
                                                     int total, int C_out, int OHW) {
-    for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
+    for (int idx = first_index(); idx < total; idx = next_index(idx, total)) {
         const int co = (idx / OHW) % C_out;
         Elem<T>::store(t2 + idx, __builtin_fmaf(Elem<T>::load(t1 + idx), scale[co], bias[co]));
     }
@@ -101,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void bn_pass(const T *__restrict__ t1, co
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void silu_pass(const T *__restrict__ t2, T *__restrict__ y, int total) {
-    for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
+    for (int idx = first_index(); idx < total; idx = next_index(idx, total)) {
         const float v = Elem<T>::load(t2 + idx);
         // SiLU alone: the epilogue helper with scale 1 and bias 0.
         Elem<T>::store(y + idx, bn_silu(v, 1.f, 0.f));

@@ -28,8 +28,10 @@
 // columns (VEC*2-byte buffer loads, zeros past the image edges and outside
 // the tensor), transposes them in registers, and writes VEC records' octets.
 // The window of the next channel block is requested while the current one is
-// multiplied; each tap's weight tile (from the packed weights, 64 contiguous
-// bytes per channel) is requested two taps ahead.
+// multiplied; each tap's weight tile is requested two taps ahead, gathered
+// straight from the OIHW weights (the 32 channels of one tap lie KH*KW
+// elements apart, so each thread assembles its two octets from 2-byte loads;
+// nothing is reordered in memory beforehand).
 //
 // Epilogue: folded BN + SiLU on the accumulators, bf16 rounding, 8-byte
 // stores of four consecutive pixels of one channel.
@@ -43,6 +45,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBN = 128;  // output channels per tile
 constexpr int kCK = 32;   // input channels per block
+
+__device__ __forceinline__ uint16_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
 
 __device__ __forceinline__ uint32_t rec_addr(uint32_t rec, uint32_t octet) {
     return rec * 64u + ((octet ^ (rec >> 1)) & 3u) * 16u;
@@ -67,7 +73,7 @@ template <> struct XV<4> {
 // FT: staging tasks per thread; FP_BYTES: LDS capacity for the window.
 template <int MBW, int VEC, int FT, int FP_BYTES, int EPI, int MIN_WG>
 __global__ __launch_bounds__(kThreads, MIN_WG) void window_bf16(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wp, const float *__restrict__ scale,
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ scale,
     const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, WinGeo g) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[FP_BYTES + 2 * kBN * 64];
     unsigned char *const fp = lds;
@@ -84,7 +90,7 @@ __global__ __launch_bounds__(kThreads, MIN_WG) void window_bf16(
     const int steps = (t_end - t_begin) * g.n_chunks;  // (tile, channel block) pairs
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.C_in * s.HW * 2u);
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)s.C_out * g.n_chunks * s.T * 64u);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)s.C_out * s.K * 2u);
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)s.N * s.C_out * s.OHW * 2u);
 
     struct Tile {
@@ -162,7 +168,9 @@ __global__ __launch_bounds__(kThreads, MIN_WG) void window_bf16(
     };
 
     // ---- weight staging: tap tile = 128 channels x 64 bytes ---------------
-    // Piece p = tid + 256*q (q = 0, 1): octet p&3 of channel p>>2.
+    // Piece p = tid + 256*q (q = 0, 1): octet p&3 of channel p>>2, i.e. the
+    // eight weights w[co][ci][tap] for ci = 32*ck + 8*(p&3) + 0..7, read as
+    // eight 2-byte loads T elements apart (zero past C_in or C_out).
     const int taps_total = steps * s.T;
     auto w_load = [&](int u, u32x4 (&reg)[2]) {
         const int step = u / s.T, tap = u - (u / s.T) * s.T;
@@ -173,9 +181,15 @@ __global__ __launch_bounds__(kThreads, MIN_WG) void window_bf16(
         for (int q = 0; q < 2; ++q) {
             const int p = tid + q * kThreads;
             const int co = co0 + (p >> 2);
+            const int ci0 = ck * kCK + 8 * (p & 3);
             const bool ok = u < taps_total && co < s.C_out;
-            reg[q] = buf_load16(wr, ok ? (uint32_t)(((co * g.n_chunks + ck) * s.T + tap) * 64 + (p & 3) * 16)
-                                       : kOOB);
+            const uint32_t base = (((uint32_t)co * (uint32_t)s.C_in + (uint32_t)ci0) * (uint32_t)s.T + (uint32_t)tap) * 2u;
+            uint16_t v[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                v[c] = buf_load2(wr, ok && ci0 + c < s.C_in ? base + (uint32_t)(c * s.T) * 2u : kOOB);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) reg[q][d] = (uint32_t)v[2 * d] | ((uint32_t)v[2 * d + 1] << 16);
         }
     };
     auto w_store = [&](int buf, const u32x4 (&reg)[2]) {
@@ -277,31 +291,6 @@ __global__ __launch_bounds__(kThreads, MIN_WG) void window_bf16(
     }
 }
 
-// Weight packing: wp[co][block][tap][c] = w[co][32*block + c][tap] (zero for
-// channels past C_in), one 16-byte octet per thread.
-__global__ __launch_bounds__(kThreads) void pack_weights_bf16(const uint16_t *__restrict__ w,
-                                                              uint16_t *__restrict__ wp, Shape s, int n_chunks) {
-    const int total = s.C_out * n_chunks * s.T * 4;
-    for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
-        const int o = idx & 3;
-        int q = idx >> 2;
-        const int tap = q % s.T;
-        q /= s.T;
-        const int ck = q % n_chunks;
-        const int co = q / n_chunks;
-        uint16_t v[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int ci = ck * kCK + 8 * o + c;
-            v[c] = ci < s.C_in ? w[(co * s.C_in + ci) * s.T + tap] : (uint16_t)0;
-        }
-        u32x4 out;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) out[d] = (uint32_t)v[2 * d] | ((uint32_t)v[2 * d + 1] << 16);
-        *(u32x4 *)(wp + (size_t)idx * 8) = out;
-    }
-}
-
 // Window capacity per instantiation (bytes of LDS for the window records).
 constexpr int kFpSmall = 56 * 1024;  // MBW = 5: two workgroups per CU
 constexpr int kFpLarge = 48 * 1024;  // MBW = 13: one workgroup per CU
@@ -370,36 +359,24 @@ bool window_supports(const Shape &s, int dtype) {
     if ((uint64_t)s.N * s.C_in * s.HW * 2 > kMaxBufferBytes ||
         (uint64_t)s.N * s.C_out * s.OHW * 2 > kMaxBufferBytes)
         return false;
-    const uint64_t wp_bytes = (uint64_t)s.C_out * ((s.C_in + kCK - 1) / kCK) * s.T * 64;
-    if (wp_bytes > kMaxBufferBytes) return false;
+    if ((uint64_t)s.C_out * s.K * 2 > kMaxBufferBytes) return false;
     WinGeo g;
     return plan(s, pick_config(s), 256, 1, &g);
 }
 
-size_t window_workspace_bytes(const Shape &s) {
-    return (size_t)s.C_out * ((s.C_in + kCK - 1) / kCK) * s.T * 64;
-}
-
-hipError_t launch_pack_weights(const Shape &s, const void *w, void *workspace, hipStream_t st) {
-    const int n_chunks = (s.C_in + kCK - 1) / kCK;
-    const int pack_total = s.C_out * n_chunks * s.T * 4;
-    const int pack_blocks = (pack_total + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(pack_weights_bf16, dim3(pack_blocks < 4096 ? pack_blocks : 4096), dim3(kThreads), 0, st,
-                       (const uint16_t *)w, (uint16_t *)workspace, s, n_chunks);
-    return hipGetLastError();
+bool window_pointers_ok(const void *x, const void *, const void *y) {
+    return (uintptr_t)x % 16 == 0 && (uintptr_t)y % 8 == 0;
 }
 
 hipError_t launch_window(const Shape &s, int epi, const void *x, const void *w, const float *scale,
-                         const float *bias, void *y, void *workspace, hipStream_t st, int num_cu) {
+                         const float *bias, void *y, hipStream_t st, int num_cu) {
     const Config &cfg = pick_config(s);
     const int wgs_per_cu = cfg.mbw == 5 ? 2 : 1;
     WinGeo g;
     if (!plan(s, cfg, num_cu, wgs_per_cu, &g)) return hipErrorInvalidValue;
-    const hipError_t e = launch_pack_weights(s, w, workspace, st);
-    if (e != hipSuccess) return e;
     const dim3 grid(g.n_wg), block(kThreads);
     auto xx = (const uint16_t *)x;
-    auto wp = (const uint16_t *)workspace;
+    auto wp = (const uint16_t *)w;
     auto yy = (uint16_t *)y;
 #define CBS_WIN(C, MIN_WG)                                                                                   \
     if (&cfg == &C) {                                                                                         \

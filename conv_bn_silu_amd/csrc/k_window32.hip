@@ -1,40 +1,58 @@
 // k_window32.hip -- implicit-GEMM 3x3 convolution on v_mfma_f32_32x32x16_bf16
-// for the compute-bound layers (many channels, small images): the input
-// window of a tile is staged in LDS once per 32-channel block and reused by
-// all nine kernel taps, as in the 16x16 window kernel, but each wave holds a
-// column of 7 32x32 accumulators so that every weight fragment read from LDS
-// feeds 7 matrix instructions ("Fusing an Epilogue", section "Three kernels
-// for one operation": the GEMM kernel has the best arithmetic intensity).
+// for the compute-bound layers (many channels, small images): the GEMM kernel
+// of "Fusing an Epilogue" (section "Three kernels for one operation": the
+// kernel that reuses each loaded value the most), with the input window of a tile
+// staged in LDS once per 16-channel chunk and reused by all nine taps, and
+// the weights read straight from their OIHW layout (no reordered copy).
 //
-// Workgroup: 8 waves (two per SIMD, so that one wave's staging and waits
-// hide behind the other's matrix work) as 2 (pixels) x 4 (channels); tile =
-// TH x TW output pixels of one image x 128 output channels; wave (wm, wn)
-// owns pixel blocks wm*MB .. wm*MB+MB-1 (32 pixels each, pixel p of the tile
-// = row p / TW, column p mod TW) and output channels 32*wn .. +31.
+// GEMM view: rows are the output pixels of a tile (TH x TW of one image, in
+// 32-pixel blocks; pixel p of the tile is row p / TW, column p mod TW),
+// columns are 128 output channels (four 32-channel blocks), and the
+// reduction runs over (16-channel chunk, tap, channel).  For a chunk the k
+// values of tap (kh, kw) at output pixel (i, j) are the 16 channels of input
+// position (i*S + kh, j*S + kw): staged once, the window serves every tap.
 //
-// Reduction order: channel block (32 channels), then groups of three taps,
-// then the tap, then two 16-channel halves.  LDS holds two window buffers
-// (this channel block and the next) and two weight buffers (this tap group
-// and the next); one barrier per tap group.  A record holds 32 channels of
-// one input position (window) or one output channel (weights) in 64 bytes,
-// padded to 80: with 5 16-byte slots per record, 16 lanes reading one slot of
-// 16 consecutive records hit 16 distinct bank groups of gfx950's 64-bank LDS,
-// and a fragment -- 8 consecutive channels of one pixel or one output
-// channel per lane -- is one ds_read_b128 whose per-tap part of the address
-// is a uniform offset.  The window's row pitch is chosen so that this holds
-// across the row wraps of the tile too.
+// Work split.  One workgroup of 4 waves per CU (one wave per SIMD), with up
+// to 14 pixel blocks x 4 channel blocks = 56 cells of 32x32 per tile.  Wave
+// (h, c) takes channel blocks 2c and 2c+1 and half h of the pixel blocks in a
+// diagonal split: numbering the cells of those two channel blocks
+// pixel-block-major, half 0 is the first PB of the 2*PB cells and half 1 the
+// rest.  With PB = 13 (a 400-pixel image fills 13 blocks; 12.5 exactly) each
+// half is 7 pixel blocks x 2 channel blocks minus one corner, so every wave
+// runs 13 matrix instructions per k step and reads 7 + 2 fragments for them
+// (each pixel fragment feeds two instructions, each weight fragment six or
+// seven).  Half 1 walks its pixel blocks from the last one down and swaps its
+// two channel blocks, so that its missing corner is the same local cell as
+// half 0's and the skip is fixed at compile time.  With PB = 14 no cell is
+// skipped.  All 13 or 14 accumulators of a wave stay in registers for the
+// whole reduction.
 //
-// Staging is through registers and runs well ahead of use: the next tap
-// group's weights (3 x 16 bytes per thread) are requested at the start of a
-// group and written at its end, and the next channel block's whole window
-// (one or two parts of 512 tasks, each task 8 channels x VEC columns,
-// transposed with byte permutes) is requested at the start of a block and
-// written at its end.  Within a group the fragment reads run a fixed
-// distance ahead of the matrix instructions.  The nine taps are unrolled with
-// the stride fixed at compile time, and blocks advance by counters, so that
-// the loop does no integer division: the scalar unit, shared by both waves
-// of a SIMD, would otherwise issue more instructions per tap than the matrix
-// core runs.
+// LDS, double buffered by chunk:
+//  * weights: [tap][channel octet][output channel] records of 16 bytes (8
+//    input channels of one output channel and tap); a pitch of 136 records
+//    per (tap, octet) keeps both the fragment reads (16 lanes on consecutive
+//    output channels) and the staging writes (8 channels x 2 octets per 16
+//    lanes) on 16 distinct bank groups.
+//  * window: [channel octet][row][position] records of 16 bytes (8 channels
+//    of one input position).  For stride 2 the columns of a row are stored
+//    even ones first, then odd ones, so that a tap's columns are consecutive.
+//    The row pitch R (records) satisfies S*R = TW (mod 16): the 16 pixels of
+//    a half-wave's fragment read then hit 16 distinct bank groups even where
+//    they wrap onto the next output row.
+// One barrier per chunk.  During chunk c the next chunk's weights and window
+// are loaded into registers (issued early in the chunk, spread between the
+// matrix instructions), transposed with byte permutes and written to the
+// other buffer late in the chunk; the barrier sits inside the chunk's last k
+// step, after which the next chunk's first fragments are read.  The
+// fragments of k step t+1 are read during k step t.
+//
+// Weight staging: thread (channel o, octet q) loads the 72 weights
+// w[co][ci0+8q .. +7][0..8] -- 144 contiguous bytes of OIHW, nine 16-byte
+// loads -- and rearranges them into nine tap records (36 byte permutes).
+//
+// Epilogue: folded BN + SiLU on the accumulators, bf16, 8-byte stores of
+// four consecutive pixels of one channel; the BN factors of the next tile are
+// loaded a tile ahead.
 #include <type_traits>
 
 #include "cbs_device.h"
@@ -44,18 +62,13 @@ namespace cbs {
 
 namespace {
 
-constexpr int kThreads32 = 512;
-constexpr int kBN32 = 128;            // output channels per tile
-constexpr int kCK32 = 32;             // input channels per block
-constexpr int kRec = 80;              // bytes per record (64 data + 16 padding)
-constexpr int kFpBytes32 = 41 * 1024; // one window buffer
-constexpr int kWTB = kBN32 * kRec;    // one tap's weights: 128 records
-constexpr int kGT = 3;                // taps per weight group (one barrier each)
-constexpr int kDepth = 4;             // fragment reads in flight ahead of the matrix instructions
-// Window staging parts of 512 tasks: one for 16-byte loads, two for 8-byte
-// loads (narrow images), which is what the register budget of two waves per
-// SIMD allows.
-constexpr int parts_for(int vec) { return vec == 8 ? 1 : 2; }
+constexpr int kThreads32 = 256;
+constexpr int kBN32 = 128;                   // output channels per tile
+constexpr int kCK32 = 16;                    // input channels per chunk
+constexpr int kPW = 136;                     // weight records per (tap, octet)
+constexpr int kWBytes = 9 * 2 * kPW * 16;    // one chunk's weights: 39,168 bytes
+constexpr int kWinBytes = 38 * 1024;         // one chunk's window, at most
+constexpr int kTasks32 = 2;                  // window staging tasks per thread, at most
 
 // Calls f(integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, typename F>
@@ -82,21 +95,30 @@ template <> struct XV32<4> {
     __device__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) { return buf_load8(r, off); }
 };
 
-// MB: 32-pixel blocks per wave; VEC: input columns per staging load (8 or
-// 4); S: stride (1 or 2).
-template <int MB, int VEC, int S, int EPI>
-__global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wp, const float *__restrict__ scale,
-    const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, WinGeo g) {
-    __shared__ __attribute__((aligned(16))) unsigned char fps[2][kFpBytes32];
-    __shared__ __attribute__((aligned(16))) unsigned char wbs[2][kGT * kWTB];
-    __shared__ __attribute__((aligned(16))) unsigned char sink[64 * 16];  // target of masked-off stores
-    typedef typename XV32<VEC>::T XT;
-    constexpr int kT = 9;  // taps
-    constexpr int kParts = parts_for(VEC);
+// Element e (0..71) of a thread's 72 weights w[co][ci0 + e/9][e%9], held as
+// nine 16-byte loads: its 32-bit word and half.
+__device__ __forceinline__ uint32_t w_word(const u32x4 (&wr)[9], int e) { return wr[e >> 3][(e >> 1) & 3]; }
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
+// VEC: input columns per window staging load (8 or 4); S: stride (1 or 2);
+// ODD: 13 pixel blocks per tile (one cell per wave skipped), else 14.
+template <int VEC, int S, bool ODD, int EPI>
+__global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ scale,
+    const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, WinGeo g) {
+    // window buffers first, so that a window fragment's address is a
+    // register plus an immediate offset below 64 KiB
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kWinBytes + 2 * kWBytes + 64 * 16];
+    unsigned char *const win = lds;
+    unsigned char *const wts = lds + 2 * kWinBytes;
+    unsigned char *const sink = lds + 2 * kWinBytes + 2 * kWBytes;  // target of masked-off stores
+    typedef typename XV32<VEC>::T XT;
+    constexpr int PBX = ODD ? 13 : 14;  // pixel blocks per tile
+    constexpr int NC = ODD ? 13 : 14;   // cells (matrix instructions per k step) per wave
+    constexpr int kT = 9;               // taps
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in scalar registers
+    const int hf = wave & 1, cp = wave >> 1;
     const int l32 = lane & 31, hi = lane >> 5;
 
     // XCD-aware placement: the XCDs take workgroups round-robin (XCD =
@@ -109,13 +131,14 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     const int t_begin = rank * g.tiles_per_wg;
     const int t_end = min(t_begin + g.tiles_per_wg, g.n_tiles);
     if (t_begin >= t_end) return;  // uniform
-    const int n_steps = (t_end - t_begin) * g.n_chunks;  // (tile, channel block) pairs
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.C_in * s.HW * 2u);
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)s.C_out * g.n_chunks * kT * 64u);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)s.C_out * s.K * 2u);
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)s.N * s.C_out * s.OHW * 2u);
+    const int R = g.row_bytes >> 4;                // window row pitch in records
+    const int plane_bytes = g.FR * g.row_bytes;    // one channel octet of the window
 
-    // A block: one 32-channel slice of one tile.
+    // A step: one 16-channel chunk of one tile.
     struct Blk {
         int tile, n, oh0, ow0, co0, ck;
         bool live;
@@ -145,36 +168,50 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         return block_at(b.tile + 1, 0, b.live && b.tile + 1 < t_end);
     };
 
-    // ---- window staging ----------------------------------------------------
-    // Task t = tid + 512 f: octet o = t&3, row parity (t>>2)&1, column group
-    // (t>>3) % ncg, row pair (t>>3) / ncg; fixed per thread, so computed once.
-    const int nparts = (((g.FR + 1) / 2) * g.ncg * 8 + kThreads32 - 1) / kThreads32;  // <= kParts
-    int tk_o[kParts], tk_cg[kParts], tk_r[kParts];
+    // ---- weight staging: thread = (output channel tid >> 1, octet tid & 1) --
+    const int wco = tid >> 1, woct = tid & 1;
+    auto w_ok = [&](const Blk &b) {
+        return b.live && b.co0 + wco < s.C_out && b.ck * kCK32 + 8 * woct < s.C_in;
+    };
+    auto w_base = [&](const Blk &b) {  // byte offset of the thread's 144-byte run
+        return (uint32_t)((b.co0 + wco) * s.C_in + b.ck * kCK32 + 8 * woct) * 18u;
+    };
+    unsigned char *const w_dst = wts + (woct * kPW + wco) * 16;
+    // record of tap t: 8 input channels c = 0..7, element c*9 + t of the run
+    auto w_record = [&](const u32x4 (&wrg)[9], int t) {
+        u32x4 v;
 #pragma unroll
-    for (int f = 0; f < kParts; ++f) {
+        for (int d = 0; d < 4; ++d) {
+            const int e0 = (2 * d) * 9 + t, e1 = e0 + 9;
+            v[d] = __builtin_amdgcn_perm(w_word(wrg, e1), w_word(wrg, e0),
+                                         ((e0 & 1) ? 0x0302u : 0x0100u) | ((e1 & 1) ? 0x07060000u : 0x05040000u));
+        }
+        return v;
+    };
+
+    // ---- window staging: task t = tid + 256 f: octet t&1, column group
+    // (t>>1) % ncg, row (t>>1) / ncg; fixed per thread ----------------------
+    int tk_o[kTasks32], tk_cg[kTasks32], tk_r[kTasks32];
+#pragma unroll
+    for (int f = 0; f < kTasks32; ++f) {
         const int t = tid + f * kThreads32;
-        const int rest = t >> 3;
-        tk_o[f] = t & 3;
-        tk_cg[f] = rest % g.ncg;
-        tk_r[f] = 2 * (rest / g.ncg) + ((t >> 2) & 1);
-        if (f >= nparts) tk_r[f] = g.FR;  // no rows: idle task
+        tk_o[f] = t & 1;
+        tk_cg[f] = (t >> 1) % g.ncg;
+        tk_r[f] = (t >> 1) / g.ncg;
+        if (tk_r[f] > g.FR) tk_r[f] = g.FR;  // no row: idle task
     }
-    // A task's 8 loads (channel c of its octet) are issued one at a time so
-    // that they can be spread between matrix instructions: fp_off gives the
-    // task's first byte offset and the number of its channels to load (0 if
-    // none).
     struct LdPlan {
         uint32_t off0;
-        int nch;
+        int nch;  // channels of the octet to load (0 if none)
     };
     auto fp_plan = [&](const Blk &b, int f) {
         const int iw_lo = b.ow0 * S - s.pad;
-        const int g0 = iw_lo & ~(VEC - 1);  // floor to a multiple of VEC
+        const int g0 = iw_lo >= 0 ? iw_lo & ~(VEC - 1) : -((-iw_lo + VEC - 1) & ~(VEC - 1));
         const int r = tk_r[f];
         const int ih = b.oh0 * S - s.pad + r;
         const int iw0 = g0 + tk_cg[f] * VEC;
         const bool ok = b.live && r < g.FR && (unsigned)ih < (unsigned)s.H && iw0 >= 0 && iw0 < s.W &&
-                        iw0 + VEC - 1 >= iw_lo && iw0 <= iw_lo + g.FC - 1;
+                        iw0 <= iw_lo + g.FC - 1;
         const int ci0 = b.ck * kCK32 + 8 * tk_o[f];
         LdPlan pl;
         pl.off0 = (uint32_t)(((b.n * s.C_in + ci0) * s.H + ih) * s.W + iw0) * 2u;
@@ -184,322 +221,370 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     auto fp_load_one = [&](const LdPlan &pl, int c) {
         return XV32<VEC>::load(xr, c < pl.nch ? pl.off0 + (uint32_t)(c * s.HW) * 2u : kOOB);
     };
-    auto fp_load = [&](const Blk &b, int f, XT (&reg)[8]) {
-        const LdPlan pl = fp_plan(b, f);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) reg[c] = fp_load_one(pl, c);
-    };
-    // Column j of a task is stored on its own, so that the stores can be
-    // spread between matrix instructions; a column outside the window (or
-    // of an idle task) goes to this lane's slot of the sink instead of
-    // branching.  c0: window column of the task's first element (> -VEC).
-    auto fp_c0 = [&](const Blk &b, int f) {
+    auto fp_c0 = [&](const Blk &b, int f) {  // window column of the task's first element (> -VEC)
         const int iw_lo = b.ow0 * S - s.pad;
-        return (iw_lo & ~(VEC - 1)) + tk_cg[f] * VEC - iw_lo;
+        const int g0 = iw_lo >= 0 ? iw_lo & ~(VEC - 1) : -((-iw_lo + VEC - 1) & ~(VEC - 1));
+        return g0 + tk_cg[f] * VEC - iw_lo;
     };
     unsigned char *const sink_lane = sink + lane * 16;
-    auto fp_store_col = [&](int c0, int f, int j, unsigned char *fp, const XT (&reg)[8]) {
+    // Column j of task f: record of its 8 channels at that column, to window
+    // position (row r, column c) of buffer `buf`, or to the sink.
+    auto fp_store_col = [&](int c0, int f, int j, unsigned char *buf, const XT (&reg)[8]) {
         const int r = tk_r[f];
         const int c = c0 + j;
-        // window column c sits at (c mod S) * CS + c / S: the columns of one
-        // phase are contiguous, so a tap's columns are consecutive
         const int pos = S == 1 ? c : (c & 1) * g.CS + (c >> 1);
         const bool ok = r < g.FR && c >= 0 && c < g.FC;
         u32x4 v;
 #pragma unroll
         for (int d = 0; d < 4; ++d) v[d] = pair16(reg[2 * d][j >> 1], reg[2 * d + 1][j >> 1], j & 1);
-        *(u32x4 *)(ok ? fp + r * g.row_bytes + tk_o[f] * 16 + pos * kRec : sink_lane) = v;
+        *(u32x4 *)(ok ? buf + tk_o[f] * plane_bytes + (r * R + pos) * 16 : sink_lane) = v;
     };
-    auto fp_store = [&](const Blk &b, int f, unsigned char *fp, const XT (&reg)[8]) {
-        const int c0 = fp_c0(b, f);
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) fp_store_col(c0, f, j, fp, reg);
-    };
-
-    // ---- weight staging: one tap x 128 channels x 4 octets; thread: channel
-    // tid >> 2, octet tid & 3 --------------------------------------------------
-    const uint32_t w_lane = (uint32_t)((tid >> 2) * g.n_chunks * kT * 64 + (tid & 3) * 16);
-    auto w_load = [&](const Blk &b, int tap) {
-        const bool ok = b.live && b.co0 + (tid >> 2) < s.C_out;
-        return buf_load16(wr, ok ? (uint32_t)((b.co0 * g.n_chunks + b.ck) * kT + tap) * 64u + w_lane : kOOB);
-    };
-    unsigned char *const w_dst = &wbs[0][0] + (tid >> 2) * kRec + (tid & 3) * 16;
 
     // ---- per-lane fragment geometry ----------------------------------------
     const int tile_px = g.TH * g.TW;
-    uint32_t abase[MB];  // byte address of this lane's pixel record (tap (0,0)), octet hi
+    uint32_t abase[7];  // window byte offset of this lane's pixel at tap (0, 0), octet hi
 #pragma unroll
-    for (int b = 0; b < MB; ++b) {
-        const int px = (wm * MB + b) * 32 + l32;
+    for (int lb = 0; lb < 7; ++lb) {
+        const int pb = hf == 0 ? lb : PBX - 1 - lb;
+        const int px = pb * 32 + l32;
         const int i = px / g.TW, j = px - (px / g.TW) * g.TW;
-        abase[b] = (uint32_t)((px < tile_px ? i * S * g.row_bytes + j * kRec : 0) + hi * 16);
+        abase[lb] = (uint32_t)(hi * plane_bytes + (px < tile_px ? (S * i * R + j) * 16 : 0));
     }
-    const uint32_t bbase = (uint32_t)((wn * 32 + l32) * kRec + hi * 16);  // weight record of this lane, octet hi
-    const int cs_b = g.CS * kRec;
-
-    f32x16 acc[MB];
+    int cbk[2];  // channel block of local column cs
+    cbk[0] = 2 * cp + (hf == 0 ? 0 : 1);
+    cbk[1] = 2 * cp + (hf == 0 ? 1 : 0);
+    uint32_t bbase[2];
 #pragma unroll
-    for (int b = 0; b < MB; ++b)
+    for (int cs = 0; cs < 2; ++cs) bbase[cs] = (uint32_t)((hi * kPW + cbk[cs] * 32 + l32) * 16);
+    int toff[kT];  // window byte offset of tap (kh, kw)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
+    for (int t = 0; t < kT; ++t) {
+        const int kh = t / 3, kw = t % 3;
+        toff[t] = (kh * R + (S == 1 ? kw : (kw & 1) * g.CS + (kw >> 1))) * 16;
+    }
 
-    // Prologue: the window of the first block and the weights of its first
-    // tap group into buffers 0.
+    // ---- prologue: the first step's weights and window into buffers 0 ------
     Blk cur = block_at(t_begin, 0, true);
     Blk nxt = next_of(cur);
-    XT fpr[kParts][8];
-    u32x4 wreg[kGT];
+    u32x4 wrg[9];
+    XT fpr[kTasks32][8];
+    {
+        const bool ok = w_ok(cur);
+        const uint32_t wb = w_base(cur);
 #pragma unroll
-    for (int t = 0; t < kGT; ++t) wreg[t] = w_load(cur, t);
-    static_for<0, kParts>([&](auto fc) {
-        constexpr int f = decltype(fc)::value;
-        fp_load(cur, f, fpr[f]);
-    });
+        for (int q = 0; q < 9; ++q) wrg[q] = buf_load16(wr, ok ? wb + 16u * q : kOOB);
 #pragma unroll
-    for (int t = 0; t < kGT; ++t) *(u32x4 *)(w_dst + t * kWTB) = wreg[t];
-    static_for<0, kParts>([&](auto fc) {
-        constexpr int f = decltype(fc)::value;
-        fp_store(cur, f, fps[0], fpr[f]);
-    });
+        for (int f = 0; f < kTasks32; ++f) {
+            const LdPlan pl = fp_plan(cur, f);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) fpr[f][c] = fp_load_one(pl, c);
+        }
+#pragma unroll
+        for (int t = 0; t < kT; ++t) *(u32x4 *)(w_dst + t * (2 * kPW * 16)) = w_record(wrg, t);
+#pragma unroll
+        for (int f = 0; f < kTasks32; ++f) {
+            const int c0 = fp_c0(cur, f);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) fp_store_col(c0, f, j, win, fpr[f]);
+        }
+    }
     __syncthreads();
 
-    // Group G (three taps; weight buffer G mod 2): request the next group's
-    // weights; run the group's 3 x 2 x MB matrix instructions with the
-    // fragment reads kDepth ahead of them, and between them write the next
-    // group's weights, in a block's first group load the next window, and in
-    // its last group write it; barrier.  The order is fixed by scheduling
-    // fences: left alone, the compiler sinks each read to just before its
-    // use, so that every instruction waits a full LDS round trip, and bunches
-    // the loads and stores, which stalls issue.
-    constexpr int kM = kGT * 2 * MB;     // matrix instructions per group
-    constexpr int kCols = kParts * VEC;  // window columns each thread stores per block
-    static_assert(kCols * 5 <= kM && 40 < kM && kParts * 16 <= kM, "staging slots exceed the group");
-    bf16x8 fa[kDepth], fb[2];
-    // BN factors of this lane's output channel, loaded a tile ahead
-    float sc_next, bi_next;
-    {
-        const int co = cur.co0 + wn * 32 + l32;
-        sc_next = co < s.C_out ? scale[co] : 0.f;
-        bi_next = co < s.C_out ? bias[co] : 0.f;
+    // Fragments: a pixel fragment is read for the next k step right after
+    // this step's last instruction that uses it (single buffer); the weight
+    // fragments, used all through a step, alternate between two sets by the
+    // parity of the k step.
+    bf16x8 fa[7], fb[2][2];
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) fb[0][cs] = *(const bf16x8 *)(wts + bbase[cs]);
+#pragma unroll
+    for (int lb = 0; lb < 7; ++lb) fa[lb] = *(const bf16x8 *)(win + abase[lb] + toff[0]);
+
+    // BN factors of this lane's two output channels, loaded a tile ahead
+    // (buffer loads: zero past C_out, without a branch)
+    const __amdgpu_buffer_rsrc_t scr = make_rsrc(scale, (uint32_t)s.C_out * 4u);
+    const __amdgpu_buffer_rsrc_t bir = make_rsrc(bias, (uint32_t)s.C_out * 4u);
+    float sc_next[2], bi_next[2];
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
+        const uint32_t off = (uint32_t)(cur.co0 + cbk[cs] * 32 + l32) * 4u;
+        sc_next[cs] = __builtin_bit_cast(float, buf_load4(scr, off));
+        bi_next[cs] = __builtin_bit_cast(float, buf_load4(bir, off));
     }
-    for (int step = 0; step < n_steps; ++step) {
-        const unsigned char *fp = fps[step & 1];
-        static_for<0, kT / kGT>([&](auto gc) {
-            constexpr int gi = decltype(gc)::value;
-            constexpr bool last_group = gi == kT / kGT - 1;
-            const int wsel = (step * (kT / kGT) + gi) & 1;
-            const unsigned char *wb = &wbs[0][0] + wsel * (kGT * kWTB);
-            unsigned char *const w_next = w_dst + (wsel ^ 1) * (kGT * kWTB);
+
+    // Slots of one chunk: slot z = k * NC + m follows matrix instruction m of
+    // k step k.  The next step's staging sits at fixed slots: weight loads in
+    // k step 0, window loads in steps 1-2, weight records written in step 4,
+    // window records in steps 6-7, the barrier after instruction 1 of step 8.
+    constexpr int zWLoad = 0;
+    constexpr int zXLoad = NC + 2;
+    constexpr int zWStore = 4 * NC;
+    constexpr int zXStore = 6 * NC + 2;
+    constexpr int zBarrier = 8 * NC + 1;
+    static_assert(zXLoad + 8 * kTasks32 <= zWStore && zWStore + 9 <= zXStore &&
+                      zXStore + kTasks32 * VEC <= zBarrier, "staging slots overlap");
+    constexpr int kLastA6 = ODD ? 12 : 13;  // instruction of the last use of pixel fragment 6
+
+    f32x16 acc[NC];
+
+    // One chunk; PAR = step parity = LDS buffer of this chunk.
+    auto chunk = [&](auto par_c) {
+        constexpr int PAR = decltype(par_c)::value;
+        // Fragment-read bases, made opaque here so that the address sums of
+        // the reads are formed next to the reads, not hoisted out of the loop
+        // into registers of their own.
+        uint32_t ab[7], bcur[2], bnxt[2];
 #pragma unroll
-            for (int t = 0; t < kGT; ++t)
-                wreg[t] = gi + 1 < kT / kGT ? w_load(cur, (gi + 1) * kGT + t) : w_load(nxt, t);
-            LdPlan lps[kParts];
-            if (gi == 0) {
+        for (int lb = 0; lb < 7; ++lb) {
+            ab[lb] = abase[lb];
+            asm volatile("" : "+v"(ab[lb]));
+        }
 #pragma unroll
-                for (int f = 0; f < kParts; ++f) lps[f] = fp_plan(nxt, f);
-            }
-            int c0s[kParts];
-            if (last_group) {
-#pragma unroll
-                for (int f = 0; f < kParts; ++f) c0s[f] = fp_c0(nxt, f);
-            }
-            unsigned char *const fp_next = fps[(step + 1) & 1];
-            // fragment m of the group: tap gi*3 + m / (2 MB), half (m / MB) % 2,
-            // pixel block m % MB; its weight fragment is read with its block 0
-            auto issue = [&](auto mc) {
-                constexpr int m = decltype(mc)::value;
-                if constexpr (m < kM) {
-                    constexpr int t = m / (2 * MB), h = (m / MB) % 2, b = m % MB;
-                    constexpr int tap = gi * kGT + t, kh = tap / 3, kw = tap % 3;
-                    if constexpr (b == 0) fb[(m / MB) % 2] = *(const bf16x8 *)(wb + t * kWTB + bbase + 32 * h);
-                    const int toff = kh * g.row_bytes + (kw % S) * cs_b + (kw / S) * kRec;
-                    fa[m % kDepth] = *(const bf16x8 *)(fp + abase[b] + toff + 32 * h);
-                }
+        for (int cs = 0; cs < 2; ++cs) {
+            bcur[cs] = 2 * kWinBytes + PAR * kWBytes + bbase[cs];
+            bnxt[cs] = 2 * kWinBytes + (PAR ^ 1) * kWBytes + bbase[cs];
+            asm volatile("" : "+v"(bcur[cs]), "+v"(bnxt[cs]));
+        }
+        unsigned char *const w_next = w_dst + (PAR ^ 1) * kWBytes;
+        unsigned char *const x_next = win + (PAR ^ 1) * kWinBytes;
+        bool wok = false;
+        uint32_t wb = 0;
+        LdPlan lps[kTasks32];
+        int c0s[kTasks32];
+        static_for<0, kT>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            constexpr int fs = (PAR + k) & 1, fn = fs ^ 1;  // weight fragment sets: this step, next step
+            constexpr bool last = k + 1 == kT;              // the next step is the next chunk's tap 0
+            constexpr int ntap = last ? 0 : k + 1;
+            constexpr int xoff = (last ? PAR ^ 1 : PAR) * kWinBytes;
+            auto rdB = [&](int cs) {
+                fb[fn][cs] = *(const bf16x8 *)(lds + (last ? bnxt[cs] : bcur[cs]) + ntap * (2 * kPW * 16));
             };
-            static_for<0, kDepth>([&](auto mc) { issue(mc); });
-            __builtin_amdgcn_sched_barrier(0);
-            static_for<0, kM>([&](auto mc) {
+            auto rdA = [&](int lb) { fa[lb] = *(const bf16x8 *)(lds + xoff + (ab[lb] + (uint32_t)toff[ntap])); };
+            if constexpr (k == 0) {
+                wok = w_ok(nxt);
+                wb = w_base(nxt);
+            }
+            if constexpr (k == 1) {
+#pragma unroll
+                for (int f = 0; f < kTasks32; ++f) lps[f] = fp_plan(nxt, f);
+            }
+            if constexpr (k == 6) {
+#pragma unroll
+                for (int f = 0; f < kTasks32; ++f) c0s[f] = fp_c0(nxt, f);
+            }
+            static_for<0, NC>([&](auto mc) {
                 constexpr int m = decltype(mc)::value;
-                constexpr int b = m % MB;
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m % kDepth], fb[(m / MB) % 2], acc[b], 0, 0, 0);
-                issue(std::integral_constant<int, m + kDepth>{});
-                // next block's window: load q (channel q mod 8 of part q / 8)
-                // after matrix instruction 2q + 1 of the first group
-                if constexpr (gi == 0 && m % 2 == 1 && m / 2 < kParts * 8) {
-                    constexpr int q = m / 2;
+                constexpr int lb = m >> 1, cs = m & 1;
+                constexpr int z = k * NC + m;
+                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[lb], fb[fs][cs], acc[m], 0, 0, 0);
+                if constexpr (z == zBarrier) __syncthreads();
+                if constexpr (m == 1) {
+                    rdB(0);
+                    rdB(1);
+                }
+                if constexpr (m % 2 == 1 && lb < 6) rdA(lb);
+                if constexpr (m == kLastA6) rdA(6);
+                if constexpr (z >= zWLoad && z < zWLoad + 9)
+                    wrg[z - zWLoad] = buf_load16(wr, wok ? wb + 16u * (z - zWLoad) : kOOB);
+                if constexpr (z >= zXLoad && z < zXLoad + 8 * kTasks32) {
+                    constexpr int q = z - zXLoad;
                     fpr[q / 8][q % 8] = fp_load_one(lps[q / 8], q % 8);
                 }
-                // next window: column q after matrix instruction 5q + 1
-                if constexpr (last_group && m % 5 == 1 && m / 5 < kCols) {
-                    constexpr int q = m / 5;
-                    fp_store_col(c0s[q / VEC], q / VEC, q % VEC, fp_next, fpr[q / VEC]);
+                if constexpr (z >= zWStore && z < zWStore + 9) {
+                    constexpr int t = z - zWStore;
+                    *(u32x4 *)(w_next + t * (2 * kPW * 16)) = w_record(wrg, t);
                 }
-                // next group's weights: tap t after matrix instruction 20 + 10 t
-                if constexpr (m >= 20 && m % 10 == 0 && (m - 20) / 10 < kGT)
-                    *(u32x4 *)(w_next + ((m - 20) / 10) * kWTB) = wreg[(m - 20) / 10];
+                if constexpr (z >= zXStore && z < zXStore + kTasks32 * VEC) {
+                    constexpr int q = z - zXStore;
+                    fp_store_col(c0s[q / VEC], q / VEC, q % VEC, x_next, fpr[q / VEC]);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
-            __syncthreads();
         });
 
-        if (cur.ck == g.n_chunks - 1) {
-            // ---- epilogue for the finished tile ----------------------------
-            // Row i = px / TW as (px * ceil(2^20 / TW)) >> 20, exact for the
-            // tile's pixels (px < 2 * MB * 32 <= 448, TW <= 448); a division
-            // would cost dozens of instructions per store.  (The tile width
-            // and its reciprocal pass through an empty asm so that the pixel
-            // coordinates are computed here, not hoisted out of the loop into
-            // registers the reduction needs.)
-            int tw_e = g.TW;
-            uint32_t rcp_tw = ((1u << 20) + (uint32_t)g.TW - 1) / (uint32_t)g.TW;
-            asm volatile("" : "+s"(tw_e), "+s"(rcp_tw));
-            const int co = cur.co0 + wn * 32 + l32;
-            const float sc = sc_next, bi = bi_next;
-            if (cur.tile + 1 < t_end) {  // the next tile's factors, ahead of its epilogue
-                const int co_n = nxt.co0 + wn * 32 + l32;
-                sc_next = co_n < s.C_out ? scale[co_n] : 0.f;
-                bi_next = co_n < s.C_out ? bias[co_n] : 0.f;
-            }
-#pragma unroll
-            for (int b = 0; b < MB; ++b) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int px = (wm * MB + b) * 32 + 8 * q + 4 * hi;
-                    const int i = (int)(((uint32_t)px * rcp_tw) >> 20), j = px - i * tw_e;
-                    const int oh = cur.oh0 + i, ow = cur.ow0 + j;
-                    const bool ok = px < tile_px && oh < s.OH && ow < s.OW && co < s.C_out;
-                    u32x2 o;
-                    const float v0 = acc[b][4 * q], v1 = acc[b][4 * q + 1];
-                    const float v2 = acc[b][4 * q + 2], v3 = acc[b][4 * q + 3];
-                    if (EPI == kFused) {
-                        o.x = pack_bf16x2(bn_silu(v0, sc, bi), bn_silu(v1, sc, bi));
-                        o.y = pack_bf16x2(bn_silu(v2, sc, bi), bn_silu(v3, sc, bi));
-                    } else {
-                        o.x = pack_bf16x2(v0, v1);
-                        o.y = pack_bf16x2(v2, v3);
-                    }
-                    buf_store8(yr, ok ? (uint32_t)(((cur.n * s.C_out + co) * s.OH + oh) * s.OW + ow) * 2u : kOOB,
-                               o);
-                }
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
-            }
-        }
         cur = nxt;
         nxt = next_of(cur);
+    };
+
+    // Tiles; per tile the accumulators start at zero, the chunks run in
+    // pairs (their count is even: a chunk past C_in adds zeros), and the
+    // epilogue follows.  (Zeroing the accumulators at the top of the tile
+    // loop, not at the end of an epilogue inside the chunk loop, keeps them
+    // in the accumulation registers across the loop.)
+    for (int tile = t_begin; tile < t_end; ++tile) {
+        const Blk tb = block_at(tile, 0, true);
+#pragma unroll
+        for (int m = 0; m < NC; ++m)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[m][e] = 0.f;
+        for (int pr = 0; pr < g.n_chunks; pr += 2) {
+            chunk(std::integral_constant<int, 0>{});
+            chunk(std::integral_constant<int, 1>{});
+        }
+
+        // ---- epilogue ----------------------------------------------------------
+        // Row i = px / TW as (px * ceil(2^20 / TW)) >> 20, exact for the
+        // tile's pixels (px < 448, TW <= 448).  The tile width, its
+        // reciprocal and the lane's own coordinates pass through an empty asm
+        // so that every pixel and channel index of the stores is computed
+        // here, not hoisted out of the loops into registers the reduction
+        // needs.
+        int tw_e = g.TW;
+        uint32_t rcp_tw = ((1u << 20) + (uint32_t)g.TW - 1) / (uint32_t)g.TW;
+        int lane_e = lane, hf_e = hf;
+        asm volatile("" : "+s"(tw_e), "+s"(rcp_tw), "+v"(lane_e), "+s"(hf_e));
+        const int l32_e = lane_e & 31, hi_e = lane_e >> 5;
+        float sc[2], bi[2];
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) {
+            sc[cs] = sc_next[cs];
+            bi[cs] = bi_next[cs];
+            // the next tile's factors, ahead of its epilogue (dropped past the
+            // last tile)
+            const uint32_t off =
+                tile + 1 < t_end ? (uint32_t)(cur.co0 + (2 * cp + (hf_e == 0 ? cs : 1 - cs)) * 32 + l32_e) * 4u : kOOB;
+            sc_next[cs] = __builtin_bit_cast(float, buf_load4(scr, off));
+            bi_next[cs] = __builtin_bit_cast(float, buf_load4(bir, off));
+        }
+        static_for<0, NC>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            constexpr int lb = m >> 1, cs = m & 1;
+            const int pb = hf_e == 0 ? lb : PBX - 1 - lb;
+            const int co = tb.co0 + (2 * cp + (hf_e == 0 ? cs : 1 - cs)) * 32 + l32_e;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int px = pb * 32 + 8 * q + 4 * hi_e;
+                const int i = (int)(((uint32_t)px * rcp_tw) >> 20), j = px - i * tw_e;
+                const int oh = tb.oh0 + i, ow = tb.ow0 + j;
+                const bool ok = (px < tile_px) & (oh < s.OH) & (ow < s.OW) & (co < s.C_out);
+                const float v0 = acc[m][4 * q], v1 = acc[m][4 * q + 1];
+                const float v2 = acc[m][4 * q + 2], v3 = acc[m][4 * q + 3];
+                u32x2 o;
+                if (EPI == kFused) {
+                    o.x = pack_bf16x2(bn_silu(v0, sc[cs], bi[cs]), bn_silu(v1, sc[cs], bi[cs]));
+                    o.y = pack_bf16x2(bn_silu(v2, sc[cs], bi[cs]), bn_silu(v3, sc[cs], bi[cs]));
+                } else {
+                    o.x = pack_bf16x2(v0, v1);
+                    o.y = pack_bf16x2(v2, v3);
+                }
+                buf_store8(yr, ok ? (uint32_t)(((tb.n * s.C_out + co) * s.OH + oh) * s.OW + ow) * 2u : kOOB, o);
+            }
+        });
     }
 }
 
-struct Config32 {
-    int mb, vec;
-};
-constexpr Config32 kW32v8{7, 8}, kW32v4{7, 4};
-
 // Window geometry of a TH x TW tile; false if it does not fit.
-bool make_geo32(const Shape &s, int TH, int TW, const Config32 &cfg, int num_cu, WinGeo *g) {
+bool make_geo32(const Shape &s, int TH, int TW, int vec, int num_cu, WinGeo *g) {
     g->TH = TH;
     g->TW = TW;
     g->FR = (TH - 1) * s.stride + s.KH;
     g->FC = (TW - 1) * s.stride + s.KW;
     g->CS = (g->FC + s.stride - 1) / s.stride;
-    g->FCP = s.stride * g->CS;
-    // Row pitch: at least the row's records, and congruent to TW * 80 / S
-    // modulo 256 / S bytes, so that output pixel (i, j) of the tile reads a
-    // record whose 16-byte bank group is 5 (i TW + j) + (a per-tap constant)
-    // mod 16: the 16 consecutive pixels of a half-wave's fragment read hit 16
-    // distinct groups of four banks even where they wrap onto the next row.
-    const int mod = 256 / s.stride;
-    const int want = (TW * kRec / s.stride) % mod;
-    int rb = g->FCP * kRec;
-    rb += ((want - rb % mod) % mod + mod) % mod;
-    g->row_bytes = rb;
-    if ((int64_t)g->FR * g->row_bytes > kFpBytes32) return false;
-    g->ncg = (g->FC - 1 + cfg.vec - 1) / cfg.vec + 1;
-    const int tasks = ((g->FR + 1) / 2) * g->ncg * 8;
-    // the next block's window is staged in at most parts_for(vec) parts of 512 tasks
-    if (tasks > parts_for(cfg.vec) * kThreads32) return false;
+    g->FCP = s.stride * g->CS;  // records a window row holds
+    // Row pitch R >= FCP with S*R = TW (mod 16) (see the file comment).
+    int R = g->FCP;
+    while ((s.stride * R - TW) % 16 != 0) ++R;
+    g->row_bytes = R * 16;
+    if ((int64_t)2 * g->FR * g->row_bytes > kWinBytes) return false;
+    g->ncg = (g->FC - 1 + vec - 1) / vec + 1;
+    // the next chunk's window is staged by at most kTasks32 tasks per thread
+    if (2 * g->FR * g->ncg > kTasks32 * kThreads32) return false;
     g->tiles_h = (s.OH + TH - 1) / TH;
     g->tiles_w = (s.OW + TW - 1) / TW;
     g->co_tiles = (s.C_out + kBN32 - 1) / kBN32;
     g->n_tiles = s.N * g->tiles_h * g->tiles_w * g->co_tiles;
     g->n_chunks = (s.C_in + kCK32 - 1) / kCK32;
+    g->n_chunks += g->n_chunks & 1;  // even: chunks run in pairs (a padding chunk adds zeros)
     g->tiles_per_wg = (g->n_tiles + num_cu - 1) / num_cu;
     g->n_wg = (g->n_tiles + g->tiles_per_wg - 1) / g->tiles_per_wg;
     return true;
 }
 
-// The tile with the most output pixels (TW a multiple of 4) whose window
-// fits; its pixels fill the 2*MB blocks of 32 as fully as possible.
-bool plan32(const Shape &s, const Config32 &cfg, int num_cu, WinGeo *g) {
-    const int max_px = 64 * cfg.mb;
-    int best = 0;
+int pixel_blocks(const WinGeo &g) { return g.TH * g.TW <= 13 * 32 ? 13 : 14; }
+
+// The tile (TW a multiple of 4, at most 448 pixels) that wastes the least
+// matrix work: the share of the computed pixel slots (tiles x 32 x pixel
+// blocks) that land on real output pixels, larger tiles on ties.  For a
+// given TW only the tallest tile that fits in 13 blocks and the tallest that
+// fits in 14 are candidates (a shorter one needs at least as many tiles), so
+// planning costs a few dozen geometry checks.
+bool plan32(const Shape &s, int vec, int num_cu, WinGeo *g) {
+    int64_t best_num = 0, best_den = 1, best_px = 0;
     WinGeo cand;
-    for (int TW = 4; TW <= s.OW && TW <= max_px; TW += 4) {
-        int TH = max_px / TW;
-        if (TH > s.OH) TH = s.OH;
-        for (; TH >= 1; --TH)
-            if (make_geo32(s, TH, TW, cfg, num_cu, &cand)) break;
-        if (TH < 1) continue;
-        // pixels computed per tile, counting the idle part of edge tiles
-        const int64_t useful = (int64_t)s.OH * s.OW;
-        const int64_t spent = (int64_t)cand.tiles_h * TH * cand.tiles_w * TW;
-        const int score = (int)((int64_t)TH * TW * useful / spent);
-        if (score > best) {
-            best = score;
-            *g = cand;
+    for (int TW = 4; TW <= s.OW && TW <= 448; TW += 4) {
+        for (int cap = 13 * 32; cap <= 14 * 32; cap += 32) {
+            int TH = min(cap / TW, s.OH);
+            while (TH >= 1 && !make_geo32(s, TH, TW, vec, num_cu, &cand)) --TH;
+            if (TH < 1) continue;
+            const int64_t useful = (int64_t)s.OH * s.OW;
+            const int64_t spent = (int64_t)cand.tiles_h * cand.tiles_w * 32 * pixel_blocks(cand);
+            const int64_t px = (int64_t)TH * TW;
+            if (useful * best_den > best_num * spent || (useful * best_den == best_num * spent && px > best_px)) {
+                best_num = useful;
+                best_den = spent;
+                best_px = px;
+                *g = cand;
+            }
         }
     }
-    return best > 0;
+    return best_num > 0;
 }
 
-const Config32 &pick32(const Shape &s) { return s.W % 8 == 0 ? kW32v8 : kW32v4; }
+int pick_vec(const Shape &s) { return s.W % 8 == 0 ? 8 : 4; }
 
 }  // namespace
 
 bool window32_supports(const Shape &s, int dtype) {
-    if (dtype != kDtypeBf16 || s.W % 4 != 0 || s.OW % 4 != 0) return false;
+    if (dtype != kDtypeBf16 || s.W % 4 != 0 || s.OW % 4 != 0 || s.C_in % 8 != 0) return false;
     if (s.KH != 3 || s.KW != 3 || (s.stride != 1 && s.stride != 2)) return false;
     if ((uint64_t)s.N * s.C_in * s.HW * 2 > kMaxBufferBytes ||
-        (uint64_t)s.N * s.C_out * s.OHW * 2 > kMaxBufferBytes)
+        (uint64_t)s.N * s.C_out * s.OHW * 2 > kMaxBufferBytes || (uint64_t)s.C_out * s.K * 2 > kMaxBufferBytes)
         return false;
-    if (window_workspace_bytes(s) > kMaxBufferBytes) return false;
     WinGeo g;
-    return plan32(s, pick32(s), 256, &g);
+    return plan32(s, pick_vec(s), 256, &g);
 }
 
-// Fraction (in 1/1000) of the matrix-core work of a tile spent on real
-// output pixels, for the dispatcher.
+bool window32_pointers_ok(const void *x, const void *w, const void *y) {
+    return (((uintptr_t)x | (uintptr_t)w) % 16 == 0) && (uintptr_t)y % 8 == 0;
+}
+
+// Share (per mille) of a tile's matrix work spent on real output pixels, for
+// the dispatcher.
 int window32_efficiency(const Shape &s) {
     WinGeo g;
-    if (!plan32(s, pick32(s), 256, &g)) return 0;
-    return (int)((int64_t)1000 * g.TH * g.TW / (64 * pick32(s).mb));
+    if (!plan32(s, pick_vec(s), 256, &g)) return 0;
+    return (int)((int64_t)1000 * s.OH * s.OW / ((int64_t)g.tiles_h * g.tiles_w * 32 * pixel_blocks(g)));
 }
 
 hipError_t launch_window32(const Shape &s, int epi, const void *x, const void *w, const float *scale,
-                           const float *bias, void *y, void *workspace, hipStream_t st, int num_cu) {
-    const Config32 &cfg = pick32(s);
+                           const float *bias, void *y, hipStream_t st, int num_cu) {
+    const int vec = pick_vec(s);
     WinGeo g;
-    if (!plan32(s, cfg, num_cu, &g)) return hipErrorInvalidValue;
-    const hipError_t e = launch_pack_weights(s, w, workspace, st);
-    if (e != hipSuccess) return e;
+    if (!plan32(s, vec, num_cu, &g)) return hipErrorInvalidValue;
+    const bool odd = pixel_blocks(g) == 13;
     const dim3 grid(g.n_wg), block(kThreads32);
     auto xx = (const uint16_t *)x;
-    auto wp = (const uint16_t *)workspace;
+    auto ww = (const uint16_t *)w;
     auto yy = (uint16_t *)y;
-#define CBS_W32(C, S_)                                                                                   \
-    if (&cfg == &C && s.stride == S_) {                                                                   \
-        if (epi == kFused)                                                                                \
-            hipLaunchKernelGGL((window32_bf16<C.mb, C.vec, S_, kFused>), grid, block, 0, st, xx, wp, scale, \
-                               bias, yy, s, g);                                                          \
-        else                                                                                              \
-            hipLaunchKernelGGL((window32_bf16<C.mb, C.vec, S_, kConvOnly>), grid, block, 0, st, xx, wp,    \
-                               scale, bias, yy, s, g);                                                   \
-        return hipGetLastError();                                                                         \
+#define CBS_W32(V, S_, O_)                                                                                  \
+    if (vec == V && s.stride == S_ && odd == O_) {                                                          \
+        if (epi == kFused)                                                                                  \
+            hipLaunchKernelGGL((window32_bf16<V, S_, O_, kFused>), grid, block, 0, st, xx, ww, scale, bias, \
+                               yy, s, g);                                                                  \
+        else                                                                                                \
+            hipLaunchKernelGGL((window32_bf16<V, S_, O_, kConvOnly>), grid, block, 0, st, xx, ww, scale,    \
+                               bias, yy, s, g);                                                            \
+        return hipGetLastError();                                                                           \
     }
-    CBS_W32(kW32v8, 1)
-    CBS_W32(kW32v4, 1)
-    CBS_W32(kW32v8, 2)
-    CBS_W32(kW32v4, 2)
+    CBS_W32(8, 1, true)
+    CBS_W32(4, 1, true)
+    CBS_W32(8, 2, true)
+    CBS_W32(4, 2, true)
+    CBS_W32(8, 1, false)
+    CBS_W32(4, 1, false)
+    CBS_W32(8, 2, false)
+    CBS_W32(4, 2, false)
 #undef CBS_W32
     return hipErrorInvalidValue;
 }

@@ -45,9 +45,10 @@ extern "C" {
 /* Status codes. */
 enum {
     CBS_OK = 0,
-    CBS_ERR_INVALID_ARG = 1, /* null pointer, bad size, unknown dtype/variant, overlap, misalignment */
-    CBS_ERR_UNSUPPORTED = 2, /* device is not gfx950, a tensor exceeds 2^31-1 elements,
-                                or a forced variant cannot run this shape */
+    CBS_ERR_INVALID_ARG = 1, /* null pointer, bad size, unknown dtype/variant, overlap */
+    CBS_ERR_UNSUPPORTED = 2, /* device is not gfx950, a tensor exceeds 2^31-1 elements, a
+                                pointer is not aligned to its element size, or a forced
+                                variant cannot run this shape or these pointers */
     CBS_ERR_NO_DEVICE = 3,   /* no HIP device is visible */
     CBS_ERR_HIP = 4,         /* a HIP runtime call failed; see conv_bn_silu_last_hip_error */
     CBS_ERR_BAD_HANDLE = 5   /* NULL, destroyed or foreign handle */
@@ -83,29 +84,30 @@ enum {
 typedef struct conv_bn_silu_handle *conv_bn_silu_t;
 
 /* Create a handle bound to the current HIP device.  Queries the device once
- * (architecture, compute-unit count) for dispatch; allocates no device memory
- * (the handle's workspace, see conv_bn_silu_run, is allocated on first use).
+ * (graphics IP version, compute-unit count) for dispatch and allocates no
+ * device memory.  The handle is read-only from then on, so one handle may
+ * serve concurrent calls from any number of threads and streams.
  * Returns CBS_ERR_NO_DEVICE without a visible device, CBS_ERR_UNSUPPORTED if
  * the device is not gfx950, CBS_ERR_INVALID_ARG if out_handle is NULL.
  * On failure *out_handle is set to NULL. */
 int conv_bn_silu_create(conv_bn_silu_t *out_handle);
 
-/* Destroy a handle.  Work already enqueued is unaffected.  NULL is accepted. */
+/* Destroy a handle.  Work already enqueued is unaffected (the kernels hold
+ * nothing of the handle).  NULL is accepted. */
 int conv_bn_silu_destroy(conv_bn_silu_t handle);
 
 /* Enqueue the fused operator on `stream` (see the conventions above).
  * N = 0 is valid and enqueues nothing (the pointers are then not looked at);
  * every other size must be >= 1, stride >= 1, pad >= 0, and the output must be non-empty.
  * y must not overlap x, w, scale or bias (the convolution reads neighbours,
- * so in-place use is not possible).  x, w and y must be aligned to their
- * element size, scale and bias to 4 bytes.
- * Workspace: variants that reorder the weights first (the window variant)
- * keep the reordered copy in a device workspace owned by the handle.  The
- * first call that needs a larger workspace than the handle holds allocates it
- * (hipMalloc; growing it first frees the old one, which waits for the
- * device); later calls allocate nothing.  Because calls share that
- * workspace, calls made with one handle must not execute concurrently: use
- * one handle per stream (or per thread) for concurrent work. */
+ * so in-place use is not possible): CBS_ERR_INVALID_ARG.  x, w and y must be
+ * aligned to their element size, scale and bias to 4 bytes, else
+ * CBS_ERR_UNSUPPORTED (16-byte alignment lets the vectorised kernels serve
+ * the call; less makes AUTO pick a kernel without vector accesses).
+ * The call allocates nothing and takes no workspace: the kernels read the
+ * weights in their OIHW layout directly.  It only enqueues kernels, so it is
+ * reentrant: calls with one handle on different streams may run
+ * concurrently. */
 int conv_bn_silu_run(conv_bn_silu_t handle,
                      const void *x, const void *w, const float *scale, const float *bias,
                      void *y,
@@ -113,7 +115,8 @@ int conv_bn_silu_run(conv_bn_silu_t handle,
                      int stride, int pad, int dtype, void *stream);
 
 /* As conv_bn_silu_run, with the kernel variant forced (CBS_VARIANT_*).  A
- * variant that cannot serve the shape or dtype returns CBS_ERR_UNSUPPORTED. */
+ * variant that cannot serve the shape, dtype or pointer alignment returns
+ * CBS_ERR_UNSUPPORTED. */
 int conv_bn_silu_run_variant(conv_bn_silu_t handle, int variant,
                              const void *x, const void *w, const float *scale, const float *bias,
                              void *y,
@@ -127,8 +130,9 @@ int conv_bn_silu_run_variant(conv_bn_silu_t handle, int variant,
  * buffers of N*C_out*OH*OW elements of `dtype` (intermediates are rounded to
  * dtype, as three separate library calls would store them).  The convolution
  * kernel is the one AUTO dispatch picks for the fused call, run without its
- * epilogue.  Same validation as conv_bn_silu_run; t1 and t2 must be aligned
- * like y and must not overlap each other or any other buffer. */
+ * epilogue.  Same validation as conv_bn_silu_run; t1 and t2 must not overlap
+ * each other or any other buffer (CBS_ERR_INVALID_ARG) and must be aligned
+ * like y (CBS_ERR_UNSUPPORTED).  Allocates nothing. */
 int conv_bn_silu_run_unfused(conv_bn_silu_t handle,
                              const void *x, const void *w, const float *scale, const float *bias,
                              void *t1, void *t2, void *y,
@@ -163,8 +167,9 @@ int conv_bn_silu_variant_supports(int variant, int N, int C_in, int H, int W, in
 const char *conv_bn_silu_status_string(int status);
 const char *conv_bn_silu_variant_name(int variant);
 
-/* The hipError_t of the last failed HIP call made through `handle`
- * (0 if none). */
+/* The hipError_t of the last failed HIP call the calling thread made through
+ * the library (0 if none; kept per thread, not in the handle, so that handles
+ * stay read-only).  0 for an invalid handle. */
 int conv_bn_silu_last_hip_error(conv_bn_silu_t handle);
 
 /* Fold inference-time batch-norm statistics into the per-channel scale and

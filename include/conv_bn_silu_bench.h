@@ -1,0 +1,43 @@
+/*
+ * conv_bn_silu_bench.h -- measurement support exported by the same library
+ * as conv_bn_silu.h: the ceilings the benchmark reports beside the published
+ * MI355X peaks, so that a layer's roofline fraction can be read against what
+ * the chip sustains in the same run.  Not part of the operator.
+ *
+ * All pointers are device pointers owned by the caller; `stream` is a
+ * hipStream_t passed as void* (NULL = the null stream).  Return values: 0 on
+ * success, 1 for an invalid argument, 3 without a device, 4 when a HIP call
+ * fails.
+ */
+#ifndef CONV_BN_SILU_BENCH_H
+#define CONV_BN_SILU_BENCH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Compute-unit count, peak shader clock (kHz) and memory clock (kHz) of the
+ * current device, as the HIP runtime reports them. */
+int conv_bn_silu_bench_device_info(int *num_cu, int *clock_khz, int *mem_clock_khz);
+
+/* The matrix-core ceiling: n_wg workgroups of 4 waves, each wave issuing
+ * `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16 on register
+ * operands (no memory access in the loop).  `sink` receives one float per
+ * thread (n_wg * 256 floats) so that the work is not optimised away.
+ * conv_bn_silu_bench_mfma_flops gives the launch's flop count (2*32*32*16
+ * per instruction), or -1 for invalid sizes. */
+int conv_bn_silu_bench_mfma(int n_wg, int iters, float *sink, void *stream);
+int64_t conv_bn_silu_bench_mfma_flops(int n_wg, int iters);
+
+/* The streaming ceiling: copy `bytes` (a multiple of 16; src and dst 16-byte
+ * aligned, not overlapping) with 16-byte loads and stores, n_wg workgroups of
+ * 256 lanes. */
+int conv_bn_silu_bench_copy(const void *src, void *dst, uint64_t bytes, int n_wg, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV_BN_SILU_BENCH_H */

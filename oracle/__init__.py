@@ -72,7 +72,7 @@ class Oracle:
 
     # -- the three passes -----------------------------------------------------
     def conv(self, x, w, stride: int, pad: int, nthreads: int = 0) -> np.ndarray:
-        """Pass 1, "conv: read x, write t1" -- cross-correlation, zero pad."""
+        """Pass 1, the convolution x -> t1: cross-correlation, zero pad."""
         x = np.ascontiguousarray(x, dtype=np.float64)
         w = np.ascontiguousarray(w, dtype=np.float64)
         N, C_in, H, W = x.shape
@@ -90,7 +90,7 @@ class Oracle:
         return t1
 
     def bn(self, t1, scale, bias) -> np.ndarray:
-        """Pass 2, "batchnorm: read t1, write t2" -- t1*scale[co] + bias[co]."""
+        """Pass 2, batch norm t1 -> t2: t1*scale[co] + bias[co]."""
         t1 = np.ascontiguousarray(t1, dtype=np.float64)
         scale = np.ascontiguousarray(scale, dtype=np.float64)
         bias = np.ascontiguousarray(bias, dtype=np.float64)
@@ -101,7 +101,7 @@ class Oracle:
         return t2
 
     def silu(self, t2) -> np.ndarray:
-        """Pass 3, "silu: read t2, write y" -- v * sigmoid(v)."""
+        """Pass 3, SiLU t2 -> y: v * sigmoid(v)."""
         t2 = np.ascontiguousarray(t2, dtype=np.float64)
         y = np.empty_like(t2)
         self._lib.cbs_oracle_silu(t2.ctypes.data, y.ctypes.data, t2.size)

@@ -6,11 +6,9 @@
  *
  * It computes the operator the slow, obvious way, in fp64, as the UNFUSED
  * three-operation sequence that "Fusing an Epilogue" (section "The problem")
- * contrasts with the fused kernel:
- *
- *     conv       read x,  write t1
- *     batchnorm  read t1, write t2
- *     silu       read t2, write y
+ * contrasts with the fused kernel: the convolution produces an intermediate
+ * t1 from x, batch norm turns t1 into a second intermediate t2, and SiLU
+ * turns t2 into the output y, each step going through memory.
  *
  * Each pass is its own function with its own output array, so a reader can
  * check every step against the page by eye.  The page states that the fused
@@ -23,7 +21,7 @@
  *     same stride and padding on both spatial axes, dilation 1, one group;
  *   - x is NCHW [N][C_in][H][W], w is OIHW [C_out][C_in][KH][KW],
  *     t1/t2/y are NCHW [N][C_out][OH][OW] with OH = floor((H+2p-KH)/s)+1;
- *   - batch norm is the folded inference form "a multiply and an add" per
+ *   - batch norm is the folded inference form, one scale and one shift per
  *     output channel: t2 = t1*scale[co] + bias[co] (order taken from the
  *     epilogue pseudocode in section "The shape of it");
  *   - sigmoid is the logistic function 1/(1+exp(-v)), and SiLU is v*sigmoid(v)
@@ -72,7 +70,7 @@ static double x_at(const double *x, int C_in, int H, int W,
     return x[(((size_t)n * C_in + ci) * H + ih) * W + iw];
 }
 
-/* Pass 1 -- convolution ("conv: read x, write t1").
+/* Pass 1 -- convolution, x to t1.
  *   t1[n][co][oh][ow] = sum_{ci<C_in} sum_{kh<KH} sum_{kw<KW}
  *                       X(n, ci, oh*s - p + kh, ow*s - p + kw) * w[co][ci][kh][kw]
  * The sum runs in the fixed order ci, kh, kw.  OpenMP splits the (n, co)
@@ -132,8 +130,8 @@ EXPORT int cbs_oracle_conv(const double *x, const double *w, double *t1,
     return 0;
 }
 
-/* Pass 2 -- folded batch norm ("batchnorm: read t1, write t2"), a multiply
- * and an add per element with the parameters of its output channel:
+/* Pass 2 -- folded batch norm, t1 to t2: each element scaled and shifted by
+ * the parameters of its output channel:
  *   t2[n][co][i] = t1[n][co][i] * scale[co] + bias[co]. */
 EXPORT void cbs_oracle_bn(const double *t1, const double *scale, const double *bias,
                           double *t2, int N, int C_out, long plane)
@@ -164,7 +162,7 @@ static double sigmoid(double v)
 #endif
 }
 
-/* Pass 3 -- SiLU ("silu: read t2, write y"): y = v * sigmoid(v).
+/* Pass 3 -- SiLU, t2 to y: y = v * sigmoid(v).
  * For v below about -709, exp(-v) overflows to +inf, sigmoid(v) = 0 and
  * y = -0.0, which is the correctly rounded limit. */
 EXPORT void cbs_oracle_silu(const double *t2, double *y, long count)

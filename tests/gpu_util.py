@@ -55,24 +55,3 @@ def oracle_full(inp: synth.Inputs) -> np.ndarray:
     import oracle
     wl = inp.wl
     return oracle.get().forward(inp.x, inp.w, inp.scale, inp.bias, wl.stride, wl.pad)
-
-
-def sample_indices(wl: synth.Workload, count: int, seed: int = 0) -> np.ndarray:
-    """Random flat NCHW output indices plus the border rows and columns of the
-    first and last plane of the first and last image."""
-    rng = np.random.default_rng(seed)
-    total = wl.N * wl.C_out * wl.OH * wl.OW
-    idx = [rng.integers(0, total, count)]
-    for n in {0, wl.N - 1}:
-        for co in {0, wl.C_out - 1}:
-            base = (n * wl.C_out + co) * wl.OH * wl.OW
-            ohs, ows = np.arange(wl.OH), np.arange(wl.OW)
-            idx += [base + ows, base + (wl.OH - 1) * wl.OW + ows, base + ohs * wl.OW,
-                    base + ohs * wl.OW + wl.OW - 1]
-    return np.unique(np.concatenate(idx)).astype(np.int64)
-
-
-def oracle_points(inp: synth.Inputs, idx: np.ndarray) -> np.ndarray:
-    import oracle
-    wl = inp.wl
-    return oracle.get().points(inp.x, inp.w, inp.scale, inp.bias, wl.stride, wl.pad, idx)

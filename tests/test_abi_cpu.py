@@ -17,14 +17,28 @@ pytestmark = pytest.mark.cpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_functions():
-    text = open(os.path.join(ROOT, "include", "conv_bn_silu.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(conv_bn_silu_\w+)\s*\(", text)))
+def declared_functions(header=None):
+    """Functions declared in include/*.h (or in one header)."""
+    names = set()
+    for h in ([header] if header else sorted(os.listdir(os.path.join(ROOT, "include")))):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(conv_bn_silu_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_and_binding_agree():
-    assert declared_functions() == sorted(B.EXPORTS)
+    assert declared_functions("conv_bn_silu.h") == sorted(B.EXPORTS)
+    assert declared_functions("conv_bn_silu_bench.h") == sorted(B.BENCH_EXPORTS)
+    assert declared_functions() == sorted(B.EXPORTS + B.BENCH_EXPORTS)
+
+
+def test_bench_helpers_without_device():
+    assert B.lib.conv_bn_silu_bench_mfma_flops(256, 10) == 256 * 4 * 10 * 8 * 2 * 32 * 32 * 16
+    assert B.lib.conv_bn_silu_bench_mfma_flops(0, 10) == -1
+    assert B.lib.conv_bn_silu_bench_copy(None, None, 16, 1, None) == 1
 
 
 @pytest.mark.parametrize("name", declared_functions())
@@ -114,17 +128,22 @@ def test_validate_null_pointers_and_empty_batch():
 
 
 def test_validate_alignment():
+    # a pointer off its element size is a well-formed call the kernels do
+    # not serve: unsupported, not invalid
     g = geo()
     p = ptrs(g)
     p[0] += 1  # bf16 x at an odd address
-    assert B.validate(*p, *g) == B.ERR_INVALID_ARG
+    assert B.validate(*p, *g) == B.ERR_UNSUPPORTED
     gf = geo(dtype=B.DTYPE_F32)
     p = ptrs(gf)
     p[4] += 2  # fp32 y at a 2-byte offset
-    assert B.validate(*p, *gf) == B.ERR_INVALID_ARG
+    assert B.validate(*p, *gf) == B.ERR_UNSUPPORTED
     p = ptrs(g)
     p[2] += 2  # scale must be 4-byte aligned
-    assert B.validate(*p, *g) == B.ERR_INVALID_ARG
+    assert B.validate(*p, *g) == B.ERR_UNSUPPORTED
+    p = ptrs(g)
+    p[1] += 2  # bf16 w at a 2-byte (element) boundary is fine
+    assert B.validate(*p, *g) == B.OK
 
 
 def test_validate_overlap():
@@ -183,3 +202,46 @@ def test_fold_bn_rejects():
         B.fold_bn(one, one, one, -one, 0.0)  # var + eps <= 0
     with pytest.raises(B.CbsError):
         B.fold_bn(one, one, one, one, -1.0)  # negative eps
+
+
+def test_misaligned_and_overlapping_reports_the_overlap():
+    # both faults at once: the overlap (a malformed call) wins
+    g = geo()
+    p = ptrs(g)
+    p[4] = p[0] + 65  # y inside x and at an odd address
+    assert B.validate(*p, *g) == B.ERR_INVALID_ARG
+
+
+def test_grid_stride_index_never_wraps():
+    """The element-wise kernels' grid-stride loop (k_scalar.hip): the next
+    index is formed in 64 bits and clamped to the total, so for every total
+    up to INT32_MAX and the largest grid the launcher uses (65536 blocks of
+    256) the sequence of indices a lane visits stays in [0, total) and ends.
+    The loop is modelled here with the same arithmetic, at the totals where
+    a 32-bit sum would wrap."""
+    stride = 65536 * 256
+    int32_max = 2**31 - 1
+    for total in (int32_max, int32_max - 1, int32_max - stride + 7, 3 * stride + 5):
+        for first in (0, 1, stride - 1):
+            idx, visits = first, 0
+            while idx < total:
+                assert 0 <= idx < total <= int32_max
+                nxt = idx + stride  # 64-bit sum
+                idx = nxt if nxt < total else total
+                visits += 1
+            assert visits == -(-(total - first) // stride)
+
+
+def test_binding_rejects_host_output_buffers():
+    """conv_bn_silu(out=...) must be a device tensor on x's device; a host
+    tensor is refused before any pointer reaches the library."""
+    import torch
+    x = torch.empty(1, 2, 4, 4, dtype=torch.float32)
+    out = torch.empty(1, 3, 4, 4, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        B._check_output(out, x, (1, 3, 4, 4), "out")
+    if not torch.cuda.is_available():
+        return
+    xd = x.cuda()
+    with pytest.raises(ValueError):
+        B._check_output(out, xd, (1, 3, 4, 4), "out")

@@ -6,7 +6,9 @@ Coverage: every variant on every shape of a sweep of small and ragged
 geometries (odd sizes, kernel sizes 1-7, strides 1-3, padding 0-3, channel
 counts off the tile sizes, M and K tails); the five workloads with a reduced
 batch checked in full; the five workloads at full size, in the launch
-configuration the benchmark times, on sampled outputs; and the degenerate
+configuration the benchmark times, every output checked; the epilogue's
+special values (SiLU(0) = 0, the closed forms, saturation to -0 and to v) on
+every variant; one handle driving two streams at once; and the degenerate
 cases (empty batch, 1x1x1, padding wider than the window's reach)."""
 import numpy as np
 import pytest
@@ -91,6 +93,13 @@ SWEEP = [
     # iterations of two rows each, and a padding row at the end for some ranks
     (6, 48, 200, 32, 64, 3, 3, 2, 1),
     (5, 16, 240, 16, 24, 3, 3, 2, 1),
+    # 32x32 window variant: more tiles than compute units (two tiles per
+    # workgroup: the tile loop and the next tile's BN factors), an odd chunk
+    # count (a padding chunk), a partial last channel tile, stride 2 with
+    # 8-column loads
+    (300, 16, 12, 12, 128, 3, 3, 1, 1),
+    (3, 48, 20, 20, 72, 3, 3, 1, 1),
+    (2, 64, 32, 32, 160, 3, 3, 2, 1),
 ]
 
 
@@ -142,16 +151,65 @@ def test_workload_reduced_full_check(lib, key, variant):
 
 
 @pytest.mark.parametrize("key", sorted(synth.WORKLOADS))
-def test_workload_full_size_sampled(lib, key):
-    """Full-size workload through AUTO dispatch (what the benchmark times):
-    sampled outputs against the oracle, every output finite."""
+def test_workload_full_size(lib, key):
+    """Each workload at its full size through AUTO dispatch -- the launch the
+    benchmark times -- with every output checked against the full oracle."""
     wl = synth.WORKLOADS[key]
     inp = synth.make_inputs(wl)
     U.say(f"[full] {key} {wl.name}")
-    y = U.to_f64(run(lib, inp)).ravel()
-    assert np.isfinite(y).all()
-    idx = U.sample_indices(wl, 6000, seed=wl.seed)
-    U.check(y[idx], U.oracle_points(inp, idx), wl.dtype, f"{key}/full")
+    y = U.to_f64(run(lib, inp))
+    U.say(f"[full] {key} oracle")
+    U.check(y, U.oracle_full(inp), wl.dtype, f"{key}/full")
+
+
+# Epilogue special values: with x = 0 the accumulator is exactly 0, so
+# v = bias[co] and y = SiLU(bias[co]) for every pixel.  The bias pattern puts
+# v at 0 (SiLU(0) = 0), +-1 and 2 (closed forms), +-20, -100, -1000 (e^-v
+# overflows: the result saturates to -0) and 1000 (e^-v underflows: y = v).
+EDGE_BIAS = [0.0, 1.0, -1.0, 2.0, 20.0, -20.0, -100.0, -1000.0, 1000.0]
+EDGE_SHAPES = [
+    # N, C_in, H, W, C_out, KH, KW, stride, pad
+    (2, 16, 9, 9, 18, 3, 3, 1, 1),      # gather, scalar
+    (2, 32, 8, 8, 20, 3, 3, 1, 1),      # window, window32
+    (2, 64, 8, 8, 40, 1, 1, 1, 0),      # pointwise
+    (2, 3, 16, 64, 16, 3, 3, 2, 1),     # small_k (stem)
+    (2, 32, 16, 64, 40, 3, 3, 2, 1),    # strided rows
+]
+
+
+def edge_cases():
+    from conv_bn_silu_amd import binding as B
+    out = []
+    for i, shp in enumerate(EDGE_SHAPES):
+        for dt in (F32, BF16):
+            for vname, v in B.VARIANTS.items():
+                if v == 0 or not B.variant_supports(v, *shp, dt):
+                    continue
+                out.append(pytest.param(i, dt, vname, id=f"e{i}-{'bf16' if dt else 'f32'}-{vname}"))
+    return out
+
+
+@pytest.mark.parametrize("case,dt,variant", edge_cases())
+def test_epilogue_special_values(lib, case, dt, variant):
+    import torch
+    N, C_in, H, W, C_out, KH, KW, s_, p_ = EDGE_SHAPES[case]
+    wl = synth.Workload(f"edge{case}", dt, N, C_in, H, W, C_out, KH, KW, s_, p_, "n01", 3000 + case)
+    inp = synth.make_inputs(wl)
+    inp.x[...] = 0.0
+    if inp.x_bits is not None:
+        inp.x_bits[...] = 0
+    inp.bias[:] = np.resize(np.array(EDGE_BIAS, np.float32), C_out)
+    U.say(f"[edge] case {case} dtype {dt} variant {variant}")
+    y = U.to_f64(run(lib, inp, variant))
+    ref = U.oracle_full(inp)
+    U.check(y, ref, dt, f"edge{case}/{variant}")
+    bias = inp.bias.astype(np.float64)[None, :, None, None] * np.ones_like(y)
+    # exact where the value is exact in the output type
+    assert np.all(y[bias == 0.0] == 0.0), "SiLU(0) must be 0"
+    assert np.all(y[bias == -1000.0] == 0.0), "SiLU(-1000) must saturate to (-)0"
+    assert np.all(y[bias == 1000.0] == 1000.0), "SiLU(1000) must be 1000"
+    assert np.all(np.abs(y[bias == -100.0]) <= 1e-30), "SiLU(-100) is below 1e-41"
+    del torch
 
 
 def test_empty_batch_is_a_no_op(lib):
@@ -200,7 +258,7 @@ def test_side_stream(lib):
     U.check(U.to_f64(y), U.oracle_full(inp), BF16, "side stream")
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5"])
 def test_unfused_sequence(lib, key):
     """The three-kernel baseline: each pass checked against the oracle's pass
     applied to the GPU's own input of that pass (so the bf16 rounding of the
@@ -218,6 +276,48 @@ def test_unfused_sequence(lib, key):
     t1h, t2h = U.to_f64(t1), U.to_f64(t2)
     U.check(t2h, o.bn(t1h, inp.scale, inp.bias), wl.dtype, "bn pass")
     U.check(U.to_f64(y), o.silu(t2h), wl.dtype, "silu pass")
+
+
+def test_one_handle_two_streams(lib):
+    """One handle, two streams, different weights and inputs on each, calls
+    interleaved so that kernels of both streams run at the same time: each
+    stream's result matches its own oracle (the handle holds no per-call
+    state, so concurrent calls cannot disturb each other)."""
+    import torch
+    h = lib.default_library()
+    inputs, uploads = [], []
+    for seed in (5101, 5102):
+        inp = synth.make_inputs(synth.WORKLOADS["c5"].with_(N=3), seed=seed)
+        inputs.append(inp)
+        uploads.append(U.upload(inp))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    torch.cuda.synchronize()
+    U.say("[streams] two streams, one handle")
+    for _ in range(4):
+        for (x, w, sc, bi), st in zip(uploads, streams):
+            with torch.cuda.stream(st):
+                outs.append(lib.conv_bn_silu(x, w, sc, bi, stride=1, pad=1, library=h))
+    torch.cuda.synchronize()
+    refs = [U.oracle_full(inp) for inp in inputs]
+    for i, y in enumerate(outs):
+        U.check(U.to_f64(y), refs[i % 2], BF16, f"stream {i % 2} call {i // 2}")
+
+
+def test_element_misaligned_pointers_are_unsupported(lib):
+    import torch
+    wl = synth.Workload("odd", BF16, 1, 8, 8, 8, 8, 3, 3, 1, 1, "n01", 4243)
+    inp = synth.make_inputs(wl)
+    x, w, sc, bi = U.upload(inp)
+    buf = torch.empty(x.numel() * 2 + 8, dtype=torch.uint8, device="cuda")
+    h = lib.default_library()
+    U.say("[misaligned] odd byte address")
+    with pytest.raises(lib.CbsError) as ei:
+        h.run_ptr(0, buf.data_ptr() + 1, w.data_ptr(), sc.data_ptr(), bi.data_ptr(),
+                  torch.empty(wl.N * wl.C_out * wl.OH * wl.OW, dtype=torch.bfloat16, device="cuda").data_ptr(),
+                  wl.N, wl.C_in, wl.H, wl.W, wl.C_out, wl.KH, wl.KW, wl.stride, wl.pad, wl.dtype,
+                  torch.cuda.current_stream().cuda_stream)
+    assert ei.value.status == lib.ERR_UNSUPPORTED
 
 
 def test_misaligned_pointers_fall_back(lib):

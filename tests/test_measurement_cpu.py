@@ -74,3 +74,29 @@ def test_bench_refuses_more_than_one_gpu():
     assert res.returncode == 2
     assert "one GPU" in res.stderr
     assert res.stdout == ""
+
+
+def test_traffic_records_are_tied_to_one_kernel_source():
+    # the digest covers the variant's own kernel file and the shared device
+    # headers only: editing another kernel leaves a record valid
+    d = {v: bench.kernel_sources_digest(v) for v in bench.VARIANT_SOURCES}
+    assert len(set(d.values())) == len(d)
+    assert all(len(x) == 16 for x in d.values())
+
+
+def test_layer_entry_fractions():
+    wl = synth.WORKLOADS["c5"]
+    kern = wl.flops / 1250e12  # half the bf16 peak
+    q = {"wl": wl, "variant": "gemm_window32", "kernel_s": kern, "wall_per_step_s": kern * 1.01,
+         "roofline": bench.roofline(wl, kern), "tflops_kernel": wl.flops / kern / 1e12,
+         "hbm_gbs_alg": wl.algorithmic_bytes / kern / 1e9}
+    e = bench.layer_entry(q, {"copy_gbs": 5000.0, "mfma_bf16_tflops": 2000.0})
+    assert e["bound"] == "mfma" and abs(e["frac"] - 0.5) < 1e-4 and abs(e["mfma_frac"] - 0.5) < 1e-4
+    assert abs(e["frac_of_mfma_ceiling"] - 0.625) < 1e-4
+    assert e["kernel_us"] <= e["wall_us_per_step"]
+
+
+def test_dispatch_sweep_shapes_are_valid():
+    from conv_bn_silu_amd import binding as B
+    for g in bench.DISPATCH_SWEEP:
+        assert B.select_variant(*g[:10]) in range(1, 8), g
