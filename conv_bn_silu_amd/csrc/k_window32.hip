@@ -12,27 +12,25 @@
 // values of tap (kh, kw) at output pixel (i, j) are the 16 channels of input
 // position (i*S + kh, j*S + kw): staged once, the window serves every tap.
 //
-// Work split.  One workgroup of 4 waves per CU (one wave per SIMD), with up
-// to 14 pixel blocks x 4 channel blocks = 56 cells of 32x32 per tile.  Wave
-// (h, c) takes channel blocks 2c and 2c+1 and half h of the pixel blocks in a
-// diagonal split: numbering the cells of those two channel blocks
-// pixel-block-major, half 0 is the first PB of the 2*PB cells and half 1 the
-// rest.  With PB = 13 (a 400-pixel image fills 13 blocks; 12.5 exactly) each
-// half is 7 pixel blocks x 2 channel blocks minus one corner, so every wave
-// runs 13 matrix instructions per k step and reads 7 + 2 fragments for them
-// (each pixel fragment feeds two instructions, each weight fragment six or
-// seven).  Half 1 walks its pixel blocks from the last one down and swaps its
-// two channel blocks, so that its missing corner is the same local cell as
-// half 0's and the skip is fixed at compile time.  With PB = 14 no cell is
-// skipped.  All 13 or 14 accumulators of a wave stay in registers for the
-// whole reduction.
+// Work split.  One workgroup of 4 waves per CU (one wave per SIMD), with 13
+// pixel blocks (up to 416 pixels: a 400-pixel image fills 12.5 of them) x 4
+// channel blocks = 52 cells of 32x32 per tile.  Wave (h, c) takes channel
+// blocks 2c and 2c+1 and half h of the pixel blocks in a diagonal split:
+// numbering the 26 cells of those two channel blocks pixel-block-major, half
+// 0 is the first 13 and half 1 the rest.  Each half is 7 pixel blocks x 2
+// channel blocks minus one corner, so every wave runs 13 matrix instructions
+// per k step and reads 7 + 2 fragments for them (each pixel fragment feeds
+// two instructions, each weight fragment six or seven).  Half 1 walks its
+// pixel blocks from the last one down and swaps its two channel blocks, so
+// that its missing corner is the same local cell as half 0's and the skip is
+// fixed at compile time.  All 13 accumulators of a wave stay in registers
+// for the whole reduction.
 //
 // LDS, double buffered by chunk:
 //  * weights: [tap][channel octet][output channel] records of 16 bytes (8
-//    input channels of one output channel and tap); a pitch of 136 records
-//    per (tap, octet) keeps both the fragment reads (16 lanes on consecutive
-//    output channels) and the staging writes (8 channels x 2 octets per 16
-//    lanes) on 16 distinct bank groups.
+//    input channels of one output channel and tap): the fragment reads and
+//    the staging writes both put 16 lanes on 16 consecutive output channels,
+//    16 distinct bank groups.
 //  * window: [channel octet][row][position] records of 16 bytes (8 channels
 //    of one input position).  For stride 2 the columns of a row are stored
 //    even ones first, then odd ones, so that a tap's columns are consecutive.
@@ -46,9 +44,12 @@
 // step, after which the next chunk's first fragments are read.  The
 // fragments of k step t+1 are read during k step t.
 //
-// Weight staging: thread (channel o, octet q) loads the 72 weights
-// w[co][ci0+8q .. +7][0..8] -- 144 contiguous bytes of OIHW, nine 16-byte
-// loads -- and rearranges them into nine tap records (36 byte permutes).
+// Weight staging: each wave loads the OIHW rows of its 32 output channels
+// for the chunk (16 channels x 9 taps = 288 contiguous bytes each) with
+// coalesced 16-byte loads -- neighbouring lanes read neighbouring pieces --
+// into a raw LDS area of its own; lane (channel o, octet q) then reads back
+// the 72 weights w[co][ci0+8q .. +7][0..8] and rearranges them into nine tap
+// records (36 byte permutes).
 //
 // Epilogue: folded BN + SiLU on the accumulators, bf16, 8-byte stores of
 // four consecutive pixels of one channel; the BN factors of the next tile are
@@ -65,9 +66,11 @@ namespace {
 constexpr int kThreads32 = 256;
 constexpr int kBN32 = 128;                   // output channels per tile
 constexpr int kCK32 = 16;                    // input channels per chunk
-constexpr int kPW = 136;                     // weight records per (tap, octet)
-constexpr int kWBytes = 9 * 2 * kPW * 16;    // one chunk's weights: 39,168 bytes
-constexpr int kWinBytes = 38 * 1024;         // one chunk's window, at most
+constexpr int kPW = 128;                     // weight records per (tap, octet)
+constexpr int kWBytes = 9 * 2 * kPW * 16;    // one chunk's weights, tap-major: 36,864 bytes
+constexpr int kRawPitch = 19 * 16;           // bytes per output channel in the raw weight area
+constexpr int kRawWave = 32 * kRawPitch;     // one wave's raw weights: 9,728 bytes
+constexpr int kWinBytes = (160 * 1024 - 2 * kWBytes - 4 * kRawWave) / 2;  // one chunk's window, at most
 constexpr int kTasks32 = 2;                  // window staging tasks per thread, at most
 
 // Calls f(integral_constant<int, I>) for I = B .. E-1.
@@ -99,21 +102,19 @@ template <> struct XV32<4> {
 // nine 16-byte loads: its 32-bit word and half.
 __device__ __forceinline__ uint32_t w_word(const u32x4 (&wr)[9], int e) { return wr[e >> 3][(e >> 1) & 3]; }
 
-// VEC: input columns per window staging load (8 or 4); S: stride (1 or 2);
-// ODD: 13 pixel blocks per tile (one cell per wave skipped), else 14.
-template <int VEC, int S, bool ODD, int EPI>
+// VEC: input columns per window staging load (8 or 4); S: stride (1 or 2).
+template <int VEC, int S, int EPI>
 __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ scale,
     const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, WinGeo g) {
     // window buffers first, so that a window fragment's address is a
     // register plus an immediate offset below 64 KiB
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kWinBytes + 2 * kWBytes + 64 * 16];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kWinBytes + 2 * kWBytes + 4 * kRawWave];
     unsigned char *const win = lds;
     unsigned char *const wts = lds + 2 * kWinBytes;
-    unsigned char *const sink = lds + 2 * kWinBytes + 2 * kWBytes;  // target of masked-off stores
     typedef typename XV32<VEC>::T XT;
-    constexpr int PBX = ODD ? 13 : 14;  // pixel blocks per tile
-    constexpr int NC = ODD ? 13 : 14;   // cells (matrix instructions per k step) per wave
+    constexpr int PBX = 13;             // pixel blocks per tile
+    constexpr int NC = 13;              // cells (matrix instructions per k step) per wave
     constexpr int kT = 9;               // taps
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -168,15 +169,28 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         return block_at(b.tile + 1, 0, b.live && b.tile + 1 < t_end);
     };
 
-    // ---- weight staging: thread = (output channel tid >> 1, octet tid & 1) --
-    const int wco = tid >> 1, woct = tid & 1;
-    auto w_ok = [&](const Blk &b) {
-        return b.live && b.co0 + wco < s.C_out && b.ck * kCK32 + 8 * woct < s.C_in;
+    // ---- weight staging: wave w stages output channels co0 + 32w .. +31 ------
+    // Loads: lane l of load q takes 16-byte piece 64q + l of the wave's 32
+    // OIHW rows of this chunk (18 pieces per output channel: 16 channels x 9
+    // taps), so each load reads a few contiguous row segments.  The pieces go
+    // to the wave's own raw area (rows padded to 19 records), and lane
+    // (channel l & 31, octet l >> 5) reads back its 144-byte run, permutes it
+    // into tap records and writes them tap-major.  All within one wave, whose
+    // LDS operations run in order, so no barrier is needed for the raw area.
+    unsigned char *const raw_w = lds + 2 * kWinBytes + 2 * kWBytes + wave * kRawWave;
+    auto w_load = [&](const Blk &b, int q) {
+        const int P = 64 * q + lane, row = P / 18, pc = P - row * 18;
+        const int co = b.co0 + 32 * wave + row;
+        const bool ok = b.live && co < s.C_out && b.ck * kCK32 + (pc >= 9 ? 8 : 0) < s.C_in;
+        return buf_load16(wr, ok ? (uint32_t)((co * s.C_in + b.ck * kCK32) * 18 + pc * 16) : kOOB);
     };
-    auto w_base = [&](const Blk &b) {  // byte offset of the thread's 144-byte run
-        return (uint32_t)((b.co0 + wco) * s.C_in + b.ck * kCK32 + 8 * woct) * 18u;
+    auto w_raw_store = [&](int q, const u32x4 &v) {
+        const int P = 64 * q + lane, row = P / 18, pc = P - row * 18;
+        *(u32x4 *)(raw_w + row * kRawPitch + pc * 16) = v;
     };
-    unsigned char *const w_dst = wts + (woct * kPW + wco) * 16;
+    const int tco = lane & 31, toct = lane >> 5;
+    auto w_raw_load = [&](int q) { return *(const u32x4 *)(raw_w + tco * kRawPitch + toct * 144 + 16 * q); };
+    unsigned char *const w_dst = wts + (toct * kPW + 32 * wave + tco) * 16;
     // record of tap t: 8 input channels c = 0..7, element c*9 + t of the run
     auto w_record = [&](const u32x4 (&wrg)[9], int t) {
         u32x4 v;
@@ -226,7 +240,9 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         const int g0 = iw_lo >= 0 ? iw_lo & ~(VEC - 1) : -((-iw_lo + VEC - 1) & ~(VEC - 1));
         return g0 + tk_cg[f] * VEC - iw_lo;
     };
-    unsigned char *const sink_lane = sink + lane * 16;
+    // masked-off stores go to the wave's raw weight area, idle while the
+    // window is written
+    unsigned char *const sink_lane = raw_w + lane * 16;
     // Column j of task f: record of its 8 channels at that column, to window
     // position (row r, column c) of buffer `buf`, or to the sink.
     auto fp_store_col = [&](int c0, int f, int j, unsigned char *buf, const XT (&reg)[8]) {
@@ -269,16 +285,18 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     u32x4 wrg[9];
     XT fpr[kTasks32][8];
     {
-        const bool ok = w_ok(cur);
-        const uint32_t wb = w_base(cur);
 #pragma unroll
-        for (int q = 0; q < 9; ++q) wrg[q] = buf_load16(wr, ok ? wb + 16u * q : kOOB);
+        for (int q = 0; q < 9; ++q) wrg[q] = w_load(cur, q);
 #pragma unroll
         for (int f = 0; f < kTasks32; ++f) {
             const LdPlan pl = fp_plan(cur, f);
 #pragma unroll
             for (int c = 0; c < 8; ++c) fpr[f][c] = fp_load_one(pl, c);
         }
+#pragma unroll
+        for (int q = 0; q < 9; ++q) w_raw_store(q, wrg[q]);
+#pragma unroll
+        for (int q = 0; q < 9; ++q) wrg[q] = w_raw_load(q);
 #pragma unroll
         for (int t = 0; t < kT; ++t) *(u32x4 *)(w_dst + t * (2 * kPW * 16)) = w_record(wrg, t);
 #pragma unroll
@@ -314,16 +332,20 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
 
     // Slots of one chunk: slot z = k * NC + m follows matrix instruction m of
     // k step k.  The next step's staging sits at fixed slots: weight loads in
-    // k step 0, window loads in steps 1-2, weight records written in step 4,
-    // window records in steps 6-7, the barrier after instruction 1 of step 8.
+    // k step 0, window loads in steps 1-2, the raw weights written in step 2
+    // and read back in step 3, tap records written in step 4, window records
+    // in steps 6-7, the barrier after instruction 1 of step 8.
     constexpr int zWLoad = 0;
     constexpr int zXLoad = NC + 2;
+    constexpr int zWRaw = 2 * NC;
+    constexpr int zWBack = 3 * NC;
     constexpr int zWStore = 4 * NC;
     constexpr int zXStore = 6 * NC + 2;
     constexpr int zBarrier = 8 * NC + 1;
-    static_assert(zXLoad + 8 * kTasks32 <= zWStore && zWStore + 9 <= zXStore &&
+    static_assert(zWLoad + 9 <= zWRaw && zWRaw + 9 <= zWBack && zWBack + 9 <= zWStore &&
+                      zXLoad + 8 * kTasks32 <= zWStore && zWStore + 9 <= zXStore &&
                       zXStore + kTasks32 * VEC <= zBarrier, "staging slots overlap");
-    constexpr int kLastA6 = ODD ? 12 : 13;  // instruction of the last use of pixel fragment 6
+    constexpr int kLastA6 = 12;  // instruction of the last use of pixel fragment 6
 
     f32x16 acc[NC];
 
@@ -347,8 +369,6 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         }
         unsigned char *const w_next = w_dst + (PAR ^ 1) * kWBytes;
         unsigned char *const x_next = win + (PAR ^ 1) * kWinBytes;
-        bool wok = false;
-        uint32_t wb = 0;
         LdPlan lps[kTasks32];
         int c0s[kTasks32];
         static_for<0, kT>([&](auto kc) {
@@ -361,10 +381,6 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
                 fb[fn][cs] = *(const bf16x8 *)(lds + (last ? bnxt[cs] : bcur[cs]) + ntap * (2 * kPW * 16));
             };
             auto rdA = [&](int lb) { fa[lb] = *(const bf16x8 *)(lds + xoff + (ab[lb] + (uint32_t)toff[ntap])); };
-            if constexpr (k == 0) {
-                wok = w_ok(nxt);
-                wb = w_base(nxt);
-            }
             if constexpr (k == 1) {
 #pragma unroll
                 for (int f = 0; f < kTasks32; ++f) lps[f] = fp_plan(nxt, f);
@@ -385,8 +401,9 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
                 }
                 if constexpr (m % 2 == 1 && lb < 6) rdA(lb);
                 if constexpr (m == kLastA6) rdA(6);
-                if constexpr (z >= zWLoad && z < zWLoad + 9)
-                    wrg[z - zWLoad] = buf_load16(wr, wok ? wb + 16u * (z - zWLoad) : kOOB);
+                if constexpr (z >= zWLoad && z < zWLoad + 9) wrg[z - zWLoad] = w_load(nxt, z - zWLoad);
+                if constexpr (z >= zWRaw && z < zWRaw + 9) w_raw_store(z - zWRaw, wrg[z - zWRaw]);
+                if constexpr (z >= zWBack && z < zWBack + 9) wrg[z - zWBack] = w_raw_load(z - zWBack);
                 if constexpr (z >= zXLoad && z < zXLoad + 8 * kTasks32) {
                     constexpr int q = z - zXLoad;
                     fpr[q / 8][q % 8] = fp_load_one(lps[q / 8], q % 8);
@@ -425,7 +442,7 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
 
         // ---- epilogue ----------------------------------------------------------
         // Row i = px / TW as (px * ceil(2^20 / TW)) >> 20, exact for the
-        // tile's pixels (px < 448, TW <= 448).  The tile width, its
+        // tile's pixels (px < 416, TW <= 416).  The tile width, its
         // reciprocal and the lane's own coordinates pass through an empty asm
         // so that every pixel and channel index of the stores is computed
         // here, not hoisted out of the loops into registers the reduction
@@ -501,34 +518,29 @@ bool make_geo32(const Shape &s, int TH, int TW, int vec, int num_cu, WinGeo *g) 
     return true;
 }
 
-int pixel_blocks(const WinGeo &g) { return g.TH * g.TW <= 13 * 32 ? 13 : 14; }
+constexpr int kTilePx = 13 * 32;  // pixels per tile, at most
 
-// The tile (TW a multiple of 4, at most 448 pixels) that wastes the least
-// matrix work: the share of the computed pixel slots (tiles x 32 x pixel
-// blocks) that land on real output pixels, larger tiles on ties.  For a
-// given TW only the tallest tile that fits in 13 blocks and the tallest that
-// fits in 14 are candidates (a shorter one needs at least as many tiles), so
-// planning costs a few dozen geometry checks.
+// The tile (TW a multiple of 4, at most 416 pixels) that wastes the least
+// matrix work: the share of the computed pixel slots (tiles x 416) that land
+// on real output pixels, larger tiles on ties.  For a given TW only the
+// tallest tile that fits is a candidate (a shorter one needs at least as
+// many tiles), so planning costs a few dozen geometry checks.
 bool plan32(const Shape &s, int vec, int num_cu, WinGeo *g) {
-    int64_t best_num = 0, best_den = 1, best_px = 0;
+    int64_t best_tiles = 0, best_px = 0;
     WinGeo cand;
-    for (int TW = 4; TW <= s.OW && TW <= 448; TW += 4) {
-        for (int cap = 13 * 32; cap <= 14 * 32; cap += 32) {
-            int TH = min(cap / TW, s.OH);
-            while (TH >= 1 && !make_geo32(s, TH, TW, vec, num_cu, &cand)) --TH;
-            if (TH < 1) continue;
-            const int64_t useful = (int64_t)s.OH * s.OW;
-            const int64_t spent = (int64_t)cand.tiles_h * cand.tiles_w * 32 * pixel_blocks(cand);
-            const int64_t px = (int64_t)TH * TW;
-            if (useful * best_den > best_num * spent || (useful * best_den == best_num * spent && px > best_px)) {
-                best_num = useful;
-                best_den = spent;
-                best_px = px;
-                *g = cand;
-            }
+    for (int TW = 4; TW <= s.OW && TW <= kTilePx; TW += 4) {
+        int TH = min(kTilePx / TW, s.OH);
+        while (TH >= 1 && !make_geo32(s, TH, TW, vec, num_cu, &cand)) --TH;
+        if (TH < 1) continue;
+        const int64_t tiles = (int64_t)cand.tiles_h * cand.tiles_w;
+        const int64_t px = (int64_t)TH * TW;
+        if (best_tiles == 0 || tiles < best_tiles || (tiles == best_tiles && px > best_px)) {
+            best_tiles = tiles;
+            best_px = px;
+            *g = cand;
         }
     }
-    return best_num > 0;
+    return best_tiles > 0;
 }
 
 int pick_vec(const Shape &s) { return s.W % 8 == 0 ? 8 : 4; }
@@ -554,7 +566,7 @@ bool window32_pointers_ok(const void *x, const void *w, const void *y) {
 int window32_efficiency(const Shape &s) {
     WinGeo g;
     if (!plan32(s, pick_vec(s), 256, &g)) return 0;
-    return (int)((int64_t)1000 * s.OH * s.OW / ((int64_t)g.tiles_h * g.tiles_w * 32 * pixel_blocks(g)));
+    return (int)((int64_t)1000 * s.OH * s.OW / ((int64_t)g.tiles_h * g.tiles_w * kTilePx));
 }
 
 hipError_t launch_window32(const Shape &s, int epi, const void *x, const void *w, const float *scale,
@@ -562,29 +574,24 @@ hipError_t launch_window32(const Shape &s, int epi, const void *x, const void *w
     const int vec = pick_vec(s);
     WinGeo g;
     if (!plan32(s, vec, num_cu, &g)) return hipErrorInvalidValue;
-    const bool odd = pixel_blocks(g) == 13;
     const dim3 grid(g.n_wg), block(kThreads32);
     auto xx = (const uint16_t *)x;
     auto ww = (const uint16_t *)w;
     auto yy = (uint16_t *)y;
-#define CBS_W32(V, S_, O_)                                                                                  \
-    if (vec == V && s.stride == S_ && odd == O_) {                                                          \
+#define CBS_W32(V, S_)                                                                                      \
+    if (vec == V && s.stride == S_) {                                                                       \
         if (epi == kFused)                                                                                  \
-            hipLaunchKernelGGL((window32_bf16<V, S_, O_, kFused>), grid, block, 0, st, xx, ww, scale, bias, \
-                               yy, s, g);                                                                  \
+            hipLaunchKernelGGL((window32_bf16<V, S_, kFused>), grid, block, 0, st, xx, ww, scale, bias, yy, \
+                               s, g);                                                                      \
         else                                                                                                \
-            hipLaunchKernelGGL((window32_bf16<V, S_, O_, kConvOnly>), grid, block, 0, st, xx, ww, scale,    \
-                               bias, yy, s, g);                                                            \
+            hipLaunchKernelGGL((window32_bf16<V, S_, kConvOnly>), grid, block, 0, st, xx, ww, scale, bias,  \
+                               yy, s, g);                                                                  \
         return hipGetLastError();                                                                           \
     }
-    CBS_W32(8, 1, true)
-    CBS_W32(4, 1, true)
-    CBS_W32(8, 2, true)
-    CBS_W32(4, 2, true)
-    CBS_W32(8, 1, false)
-    CBS_W32(4, 1, false)
-    CBS_W32(8, 2, false)
-    CBS_W32(4, 2, false)
+    CBS_W32(8, 1)
+    CBS_W32(4, 1)
+    CBS_W32(8, 2)
+    CBS_W32(4, 2)
 #undef CBS_W32
     return hipErrorInvalidValue;
 }
