@@ -9,9 +9,12 @@ reports them under "layers".  Input/output buffer sets are rotated so that
 the working set of consecutive steps exceeds twice the 256 MB Infinity Cache
 and every step streams from HBM.
 
-Timing: W untimed warm-up steps, then exactly K steps in one timed region,
-bracketed by torch.cuda.synchronize() on both sides, with a HIP event pair on
-the launch stream around the same K launches.  value and ms_per_step come
+Timing: the layer's own step repeated untimed for at least --settle-ms (the
+GPU's clocks ramp up over the first tens of milliseconds of load; without
+this the first layer of a short run measures the ramp), then W untimed
+warm-up steps, then exactly K steps in one timed region, bracketed by
+torch.cuda.synchronize() on both sides, with a HIP event pair on the launch
+stream around the same K launches.  value and ms_per_step come
 from the wall clock of that region; the roofline's "achieved" from the event
 pair (the kernel's average launch duration), so the kernel time per step is
 never above ms_per_step.
@@ -123,11 +126,21 @@ class Layer:
         self.geo = (wl.N, wl.C_in, wl.H, wl.W, wl.C_out, wl.KH, wl.KW, wl.stride, wl.pad, wl.dtype)
 
 
+SETTLE_S = 0.3
+
+
 def timed_region(step, steps: int, warmup: int, stream) -> dict:
-    """W warm-up steps, then exactly `steps` steps in one region bracketed by
-    device synchronisation, with a HIP event pair on the launch stream around
-    the same launches."""
+    """The step repeated untimed for SETTLE_S seconds, W warm-up steps, then
+    exactly `steps` steps in one region bracketed by device synchronisation,
+    with a HIP event pair on the launch stream around the same launches."""
     import torch
+    t_settle = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(32):  # batches keep the GPU loaded without a deep queue
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(warmup):
         step(i)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -425,6 +438,8 @@ def main():
     ap.add_argument("--variants", action="store_true", help="also check the dispatch on a shape sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed repetitions of each layer's step before its warm-up (clock ramp)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -443,6 +458,8 @@ def main():
         copy_calibration(args.copy_calibration, max(1, args.steps))
         return
     from conv_bn_silu_amd import synth
+    global SETTLE_S
+    SETTLE_S = args.settle_ms / 1000.0
     wl = synth.WORKLOADS[args.workload]
     dev = device_info()
     num_cu = dev.get("num_cu", 256)
@@ -469,6 +486,7 @@ def main():
                    "KH": wl.KH, "KW": wl.KW, "stride": wl.stride, "pad": wl.pad, "variant": r["variant"],
                    "rotated_buffer_sets": r["sets"], "kernel_us_mean": round(r["kernel_s"] * 1e6, 3),
                    "host_issue_us_per_step": round(r["host_issue_us_per_step"], 3),
+                   "settle_ms": args.settle_ms,
                    "algorithmic_bytes": wl.algorithmic_bytes, "flops": wl.flops, **dev},
         "roofline": roof,
     }

@@ -181,8 +181,12 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     auto w_load = [&](const Blk &b, int q) {
         const int P = 64 * q + lane, row = P / 18, pc = P - row * 18;
         const int co = b.co0 + 32 * wave + row;
-        const bool ok = b.live && co < s.C_out && b.ck * kCK32 + (pc >= 9 ? 8 : 0) < s.C_in;
-        return buf_load16(wr, ok ? (uint32_t)((co * s.C_in + b.ck * kCK32) * 18 + pc * 16) : kOOB);
+        const bool ok = b.live & (co < s.C_out) & (b.ck * kCK32 + (pc >= 9 ? 8 : 0) < s.C_in);
+        // the offset is formed for every lane and then selected: left to
+        // itself the compiler guards the multiply with a branch per load
+        uint32_t off = (uint32_t)((co * s.C_in + b.ck * kCK32) * 18 + pc * 16);
+        asm("" : "+v"(off));
+        return buf_load16(wr, ok ? off : kOOB);
     };
     auto w_raw_store = [&](int q, const u32x4 &v) {
         const int P = 64 * q + lane, row = P / 18, pc = P - row * 18;
@@ -224,8 +228,8 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         const int r = tk_r[f];
         const int ih = b.oh0 * S - s.pad + r;
         const int iw0 = g0 + tk_cg[f] * VEC;
-        const bool ok = b.live && r < g.FR && (unsigned)ih < (unsigned)s.H && iw0 >= 0 && iw0 < s.W &&
-                        iw0 <= iw_lo + g.FC - 1;
+        const bool ok = b.live & (r < g.FR) & ((unsigned)ih < (unsigned)s.H) & (iw0 >= 0) & (iw0 < s.W) &
+                        (iw0 <= iw_lo + g.FC - 1);
         const int ci0 = b.ck * kCK32 + 8 * tk_o[f];
         LdPlan pl;
         pl.off0 = (uint32_t)(((b.n * s.C_in + ci0) * s.H + ih) * s.W + iw0) * 2u;
@@ -332,18 +336,19 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
 
     // Slots of one chunk: slot z = k * NC + m follows matrix instruction m of
     // k step k.  The next step's staging sits at fixed slots: weight loads in
-    // k step 0, window loads in steps 1-2, the raw weights written in step 2
-    // and read back in step 3, tap records written in step 4, window records
-    // in steps 6-7, the barrier after instruction 1 of step 8.
+    // k step 0, window loads in steps 1-2, the raw weights written in step 4
+    // (four steps after their loads) and read back right after, tap records
+    // written in step 5, window records in steps 6-7, the barrier after
+    // instruction 1 of step 8.
     constexpr int zWLoad = 0;
     constexpr int zXLoad = NC + 2;
-    constexpr int zWRaw = 2 * NC;
-    constexpr int zWBack = 3 * NC;
-    constexpr int zWStore = 4 * NC;
+    constexpr int zWRaw = 4 * NC;
+    constexpr int zWBack = 4 * NC + 9;
+    constexpr int zWStore = 5 * NC + 5;
     constexpr int zXStore = 6 * NC + 2;
     constexpr int zBarrier = 8 * NC + 1;
     static_assert(zWLoad + 9 <= zWRaw && zWRaw + 9 <= zWBack && zWBack + 9 <= zWStore &&
-                      zXLoad + 8 * kTasks32 <= zWStore && zWStore + 9 <= zXStore &&
+                      zXLoad + 8 * kTasks32 <= zWRaw && zWStore + 9 <= zXStore &&
                       zXStore + kTasks32 * VEC <= zBarrier, "staging slots overlap");
     constexpr int kLastA6 = 12;  // instruction of the last use of pixel fragment 6
 
