@@ -44,6 +44,13 @@
 // step, after which the next chunk's first fragments are read.  The
 // fragments of k step t+1 are read during k step t.
 //
+// Window staging: a task is 8 channels x 8 columns of one input row -- eight
+// 16-byte loads, one per channel -- transposed into 8 position records with
+// byte permutes.  Where W = 4 mod 8 the rows start on 8-byte boundaries and a
+// row's last group reads 4 elements of the next row; those columns are zeroed
+// when the records are formed (zeroing them at the load would make every
+// load wait for its data on the spot).
+//
 // Weight staging: each wave loads the OIHW rows of its 32 output channels
 // for the chunk (16 channels x 9 taps = 288 contiguous bytes each) with
 // coalesced 16-byte loads -- neighbouring lanes read neighbouring pieces --
@@ -59,6 +66,7 @@
 #include "cbs_device.h"
 #include "cbs_launch.h"
 
+
 namespace cbs {
 
 namespace {
@@ -71,7 +79,8 @@ constexpr int kWBytes = 9 * 2 * kPW * 16;    // one chunk's weights, tap-major: 
 constexpr int kRawPitch = 19 * 16;           // bytes per output channel in the raw weight area
 constexpr int kRawWave = 32 * kRawPitch;     // one wave's raw weights: 9,728 bytes
 constexpr int kWinBytes = (160 * 1024 - 2 * kWBytes - 4 * kRawWave) / 2;  // one chunk's window, at most
-constexpr int kTasks32 = 2;                  // window staging tasks per thread, at most
+constexpr int kMaxTasks32 = 2;               // window staging tasks per thread, at most
+constexpr int kVec = 8;                      // input columns per window staging load
 
 // Calls f(integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, typename F>
@@ -88,22 +97,12 @@ __device__ __forceinline__ uint32_t pair16(uint32_t lo_word, uint32_t hi_word, i
     return __builtin_amdgcn_perm(hi_word, lo_word, h == 0 ? 0x05040100u : 0x07060302u);
 }
 
-template <int VEC> struct XV32;
-template <> struct XV32<8> {
-    typedef u32x4 T;
-    __device__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) { return buf_load16(r, off); }
-};
-template <> struct XV32<4> {
-    typedef u32x2 T;
-    __device__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) { return buf_load8(r, off); }
-};
-
 // Element e (0..71) of a thread's 72 weights w[co][ci0 + e/9][e%9], held as
 // nine 16-byte loads: its 32-bit word and half.
 __device__ __forceinline__ uint32_t w_word(const u32x4 (&wr)[9], int e) { return wr[e >> 3][(e >> 1) & 3]; }
 
-// VEC: input columns per window staging load (8 or 4); S: stride (1 or 2).
-template <int VEC, int S, int EPI>
+// S: stride (1 or 2); TASKS: window staging tasks per thread (1 or 2).
+template <int S, int TASKS, int EPI>
 __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ scale,
     const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, WinGeo g) {
@@ -112,7 +111,9 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kWinBytes + 2 * kWBytes + 4 * kRawWave];
     unsigned char *const win = lds;
     unsigned char *const wts = lds + 2 * kWinBytes;
-    typedef typename XV32<VEC>::T XT;
+    constexpr int VEC = kVec;
+    constexpr int kTasks32 = TASKS;
+    typedef u32x4 XT;
     constexpr int PBX = 13;             // pixel blocks per tile
     constexpr int NC = 13;              // cells (matrix instructions per k step) per wave
     constexpr int kT = 9;               // taps
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     }
     struct LdPlan {
         uint32_t off0;
-        int nch;  // channels of the octet to load (0 if none)
+        int nch;    // channels of the octet to load (0 if none)
     };
     auto fp_plan = [&](const Blk &b, int f) {
         const int iw_lo = b.ow0 * S - s.pad;
@@ -236,8 +237,11 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         pl.nch = ok ? min(8, s.C_in - ci0) : 0;
         return pl;
     };
+    // 16-byte loads of 8 columns; rows of W = 4 mod 8 start 8-byte aligned,
+    // and the last group of such a row reads 4 elements of the next row,
+    // which are zeroed here
     auto fp_load_one = [&](const LdPlan &pl, int c) {
-        return XV32<VEC>::load(xr, c < pl.nch ? pl.off0 + (uint32_t)(c * s.HW) * 2u : kOOB);
+        return buf_load16(xr, c < pl.nch ? pl.off0 + (uint32_t)(c * s.HW) * 2u : kOOB);
     };
     auto fp_c0 = [&](const Blk &b, int f) {  // window column of the task's first element (> -VEC)
         const int iw_lo = b.ow0 * S - s.pad;
@@ -249,7 +253,12 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     unsigned char *const sink_lane = raw_w + lane * 16;
     // Column j of task f: record of its 8 channels at that column, to window
     // position (row r, column c) of buffer `buf`, or to the sink.
-    auto fp_store_col = [&](int c0, int f, int j, unsigned char *buf, const XT (&reg)[8]) {
+    auto fp_edge = [&](const Blk &b, int f) {  // the task's group runs past the row end
+        const int iw_lo = b.ow0 * S - s.pad;
+        const int g0 = iw_lo >= 0 ? iw_lo & ~(VEC - 1) : -((-iw_lo + VEC - 1) & ~(VEC - 1));
+        return g0 + tk_cg[f] * VEC + VEC > s.W;
+    };
+    auto fp_store_col = [&](int c0, bool edge_f, int f, int j, unsigned char *buf, const XT (&reg)[8]) {
         const int r = tk_r[f];
         const int c = c0 + j;
         const int pos = S == 1 ? c : (c & 1) * g.CS + (c >> 1);
@@ -257,6 +266,10 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         u32x4 v;
 #pragma unroll
         for (int d = 0; d < 4; ++d) v[d] = pair16(reg[2 * d][j >> 1], reg[2 * d + 1][j >> 1], j & 1);
+        if (j >= 4) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) v[d] = edge_f ? 0u : v[d];
+        }
         *(u32x4 *)(ok ? buf + tk_o[f] * plane_bytes + (r * R + pos) * 16 : sink_lane) = v;
     };
 
@@ -306,8 +319,9 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
 #pragma unroll
         for (int f = 0; f < kTasks32; ++f) {
             const int c0 = fp_c0(cur, f);
+            const bool e = fp_edge(cur, f);
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) fp_store_col(c0, f, j, win, fpr[f]);
+            for (int j = 0; j < VEC; ++j) fp_store_col(c0, e, f, j, win, fpr[f]);
         }
     }
     __syncthreads();
@@ -376,6 +390,7 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         unsigned char *const x_next = win + (PAR ^ 1) * kWinBytes;
         LdPlan lps[kTasks32];
         int c0s[kTasks32];
+        bool eds[kTasks32];
         static_for<0, kT>([&](auto kc) {
             constexpr int k = decltype(kc)::value;
             constexpr int fs = (PAR + k) & 1, fn = fs ^ 1;  // weight fragment sets: this step, next step
@@ -392,7 +407,10 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
             }
             if constexpr (k == 6) {
 #pragma unroll
-                for (int f = 0; f < kTasks32; ++f) c0s[f] = fp_c0(nxt, f);
+                for (int f = 0; f < kTasks32; ++f) {
+                    c0s[f] = fp_c0(nxt, f);
+                    eds[f] = fp_edge(nxt, f);
+                }
             }
             static_for<0, NC>([&](auto mc) {
                 constexpr int m = decltype(mc)::value;
@@ -419,7 +437,7 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
                 }
                 if constexpr (z >= zXStore && z < zXStore + kTasks32 * VEC) {
                     constexpr int q = z - zXStore;
-                    fp_store_col(c0s[q / VEC], q / VEC, q % VEC, x_next, fpr[q / VEC]);
+                    fp_store_col(c0s[q / VEC], eds[q / VEC], q / VEC, q % VEC, x_next, fpr[q / VEC]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -511,7 +529,7 @@ bool make_geo32(const Shape &s, int TH, int TW, int vec, int num_cu, WinGeo *g) 
     if ((int64_t)2 * g->FR * g->row_bytes > kWinBytes) return false;
     g->ncg = (g->FC - 1 + vec - 1) / vec + 1;
     // the next chunk's window is staged by at most kTasks32 tasks per thread
-    if (2 * g->FR * g->ncg > kTasks32 * kThreads32) return false;
+    if (2 * g->FR * g->ncg > kMaxTasks32 * kThreads32) return false;
     g->tiles_h = (s.OH + TH - 1) / TH;
     g->tiles_w = (s.OW + TW - 1) / TW;
     g->co_tiles = (s.C_out + kBN32 - 1) / kBN32;
@@ -548,7 +566,6 @@ bool plan32(const Shape &s, int vec, int num_cu, WinGeo *g) {
     return best_tiles > 0;
 }
 
-int pick_vec(const Shape &s) { return s.W % 8 == 0 ? 8 : 4; }
 
 }  // namespace
 
@@ -559,7 +576,7 @@ bool window32_supports(const Shape &s, int dtype) {
         (uint64_t)s.N * s.C_out * s.OHW * 2 > kMaxBufferBytes || (uint64_t)s.C_out * s.K * 2 > kMaxBufferBytes)
         return false;
     WinGeo g;
-    return plan32(s, pick_vec(s), 256, &g);
+    return plan32(s, kVec, 256, &g);
 }
 
 bool window32_pointers_ok(const void *x, const void *w, const void *y) {
@@ -570,33 +587,33 @@ bool window32_pointers_ok(const void *x, const void *w, const void *y) {
 // the dispatcher.
 int window32_efficiency(const Shape &s) {
     WinGeo g;
-    if (!plan32(s, pick_vec(s), 256, &g)) return 0;
+    if (!plan32(s, kVec, 256, &g)) return 0;
     return (int)((int64_t)1000 * s.OH * s.OW / ((int64_t)g.tiles_h * g.tiles_w * kTilePx));
 }
 
 hipError_t launch_window32(const Shape &s, int epi, const void *x, const void *w, const float *scale,
                            const float *bias, void *y, hipStream_t st, int num_cu) {
-    const int vec = pick_vec(s);
     WinGeo g;
-    if (!plan32(s, vec, num_cu, &g)) return hipErrorInvalidValue;
+    if (!plan32(s, kVec, num_cu, &g)) return hipErrorInvalidValue;
+    const int tasks = 2 * g.FR * g.ncg <= kThreads32 ? 1 : 2;
     const dim3 grid(g.n_wg), block(kThreads32);
     auto xx = (const uint16_t *)x;
     auto ww = (const uint16_t *)w;
     auto yy = (uint16_t *)y;
-#define CBS_W32(V, S_)                                                                                      \
-    if (vec == V && s.stride == S_) {                                                                       \
+#define CBS_W32(S_, T_)                                                                                     \
+    if (s.stride == S_ && tasks == T_) {                                                                    \
         if (epi == kFused)                                                                                  \
-            hipLaunchKernelGGL((window32_bf16<V, S_, kFused>), grid, block, 0, st, xx, ww, scale, bias, yy, \
+            hipLaunchKernelGGL((window32_bf16<S_, T_, kFused>), grid, block, 0, st, xx, ww, scale, bias, yy, \
                                s, g);                                                                      \
         else                                                                                                \
-            hipLaunchKernelGGL((window32_bf16<V, S_, kConvOnly>), grid, block, 0, st, xx, ww, scale, bias,  \
+            hipLaunchKernelGGL((window32_bf16<S_, T_, kConvOnly>), grid, block, 0, st, xx, ww, scale, bias,  \
                                yy, s, g);                                                                  \
         return hipGetLastError();                                                                           \
     }
-    CBS_W32(8, 1)
-    CBS_W32(4, 1)
-    CBS_W32(8, 2)
-    CBS_W32(4, 2)
+    CBS_W32(1, 1)
+    CBS_W32(1, 2)
+    CBS_W32(2, 1)
+    CBS_W32(2, 2)
 #undef CBS_W32
     return hipErrorInvalidValue;
 }
