@@ -29,7 +29,7 @@ VARIANTS = {"auto": 0, "gemm_gather": 1, "gemm_window": 2, "pointwise": 3, "smal
 # library exports each.
 EXPORTS = [
     "conv_bn_silu_create", "conv_bn_silu_destroy", "conv_bn_silu_run", "conv_bn_silu_run_variant",
-    "conv_bn_silu_run_unfused", "conv_bn_silu_output_hw", "conv_bn_silu_validate",
+    "conv_bn_silu_run_unfused", "conv_bn_silu_run_unfused_noalloc", "conv_bn_silu_output_hw", "conv_bn_silu_validate",
     "conv_bn_silu_select_variant", "conv_bn_silu_variant_supports", "conv_bn_silu_status_string",
     "conv_bn_silu_variant_name", "conv_bn_silu_last_hip_error", "conv_bn_silu_fold_bn",
 ]
@@ -62,6 +62,7 @@ def _load() -> ctypes.CDLL:
     lib.conv_bn_silu_run.argtypes = [vp, vp, vp, vp, vp, vp] + geo + [vp]
     lib.conv_bn_silu_run_variant.argtypes = [vp, i, vp, vp, vp, vp, vp] + geo + [vp]
     lib.conv_bn_silu_run_unfused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp] + geo + [vp]
+    lib.conv_bn_silu_run_unfused_noalloc.argtypes = [vp, vp, vp, vp, vp, vp] + geo + [vp]
     lib.conv_bn_silu_output_hw.argtypes = [i] * 6 + [ip, ip]
     lib.conv_bn_silu_validate.argtypes = [vp, vp, vp, vp, vp] + geo
     lib.conv_bn_silu_select_variant.argtypes = geo + [i]
@@ -168,6 +169,12 @@ class Library:
                                                  C_out, KH, KW, stride, pad, dtype, stream),
                     "conv_bn_silu_run_variant")
 
+    def run_unfused_noalloc_ptr(self, x, w, scale, bias, y, N, C_in, H, W, C_out, KH, KW, stride, pad, dtype,
+                                stream):
+        self._check(lib.conv_bn_silu_run_unfused_noalloc(self.handle, x, w, scale, bias, y, N, C_in, H, W, C_out,
+                                                         KH, KW, stride, pad, dtype, stream),
+                    "conv_bn_silu_run_unfused_noalloc")
+
     def run_unfused_ptr(self, x, w, scale, bias, t1, t2, y, N, C_in, H, W, C_out, KH, KW, stride, pad, dtype,
                         stream):
         self._check(lib.conv_bn_silu_run_unfused(self.handle, x, w, scale, bias, t1, t2, y, N, C_in, H, W,
@@ -250,3 +257,19 @@ def conv_bn_silu_unfused(x, w, scale, bias, stride: int = 1, pad: int = 0, libra
     lib_.run_unfused_ptr(x.data_ptr(), w.data_ptr(), scale.data_ptr(), bias.data_ptr(), t1.data_ptr(),
                          t2.data_ptr(), y.data_ptr(), *geo, stream)
     return y, t1, t2
+
+
+def conv_bn_silu_unfused_noalloc(x, w, scale, bias, stride: int = 1, pad: int = 0, out=None,
+                                 library: Library | None = None):
+    """The unfused sequence with its intermediates in the library's static
+    device scratch (conv_bn_silu_run_unfused_noalloc); returns y.  With
+    `out` given, nothing is allocated."""
+    import torch
+    geo, yshape = _geometry(x, w, scale, bias, stride, pad)
+    y = torch.empty(yshape, dtype=x.dtype, device=x.device) if out is None else out
+    _check_output(y, x, yshape, "out")
+    lib_ = library or default_library()
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    lib_.run_unfused_noalloc_ptr(x.data_ptr(), w.data_ptr(), scale.data_ptr(), bias.data_ptr(), y.data_ptr(),
+                                 *geo, stream)
+    return y

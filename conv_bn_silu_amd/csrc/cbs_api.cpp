@@ -21,6 +21,9 @@ struct conv_bn_silu_handle {
     // concurrent calls from any number of threads and streams.
     int device;
     int num_cu;
+    // Device address of the allocation-free entry point's scratch on this
+    // device (NULL if the lookup failed; that entry point then reports it).
+    void *noalloc_scratch;
 };
 
 namespace {
@@ -187,6 +190,20 @@ int prologue(conv_bn_silu_t h, const void *x, const void *w, const float *scale,
     return CBS_OK;
 }
 
+// The unfused sequence on t1, t2 (validated by the caller): the AUTO
+// variant's convolution without its epilogue, then the BN pass, then SiLU.
+int launch_unfused(const conv_bn_silu_handle *h, const cbs::Shape &s, int dtype, const void *x, const void *w,
+                   const float *scale, const float *bias, void *t1, void *t2, void *y, hipStream_t st) {
+    const int variant = select_for_call(s, dtype, h->num_cu, x, w, t1);
+    int rc = record_hip(launch(variant, s, dtype, cbs::kConvOnly, x, w, scale, bias, t1, st, h->num_cu));
+    if (rc != CBS_OK) return rc;
+    (void)hipGetLastError();
+    rc = record_hip(cbs::launch_bn_pass(s, dtype, t1, scale, bias, t2, st));
+    if (rc != CBS_OK) return rc;
+    (void)hipGetLastError();
+    return record_hip(cbs::launch_silu_pass(s, dtype, t2, y, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -209,6 +226,9 @@ int conv_bn_silu_create(conv_bn_silu_t *out_handle) {
     auto *h = new conv_bn_silu_handle;
     h->device = dev;
     h->num_cu = num_cu;
+    h->noalloc_scratch = nullptr;
+    if (cbs::noalloc_scratch_address(&h->noalloc_scratch) != hipSuccess) h->noalloc_scratch = nullptr;
+    (void)hipGetLastError();
     {
         std::lock_guard<std::mutex> lk(g_handles_mu);
         g_handles.insert(h);
@@ -268,15 +288,23 @@ int conv_bn_silu_run_unfused(conv_bn_silu_t h, const void *x, const void *w, con
     for (const Range &o : others)
         if (overlap(r1, o) || overlap(r2, o)) return CBS_ERR_INVALID_ARG;
     if (((uintptr_t)t1 | (uintptr_t)t2) % e != 0) return CBS_ERR_UNSUPPORTED;
-    const hipStream_t st = (hipStream_t)stream;
-    const int variant = select_for_call(s, dtype, h->num_cu, x, w, t1);
-    rc = record_hip(launch(variant, s, dtype, cbs::kConvOnly, x, w, scale, bias, t1, st, h->num_cu));
+    return launch_unfused(h, s, dtype, x, w, scale, bias, t1, t2, y, (hipStream_t)stream);
+}
+
+int conv_bn_silu_run_unfused_noalloc(conv_bn_silu_t h, const void *x, const void *w, const float *scale,
+                                     const float *bias, void *y, int N, int C_in, int H, int W, int C_out, int KH,
+                                     int KW, int stride, int pad, int dtype, void *stream) {
+    cbs::Shape s;
+    const int rc = prologue(h, x, w, scale, bias, y, N, C_in, H, W, C_out, KH, KW, stride, pad, dtype, &s);
     if (rc != CBS_OK) return rc;
-    (void)hipGetLastError();
-    rc = record_hip(cbs::launch_bn_pass(s, dtype, t1, scale, bias, t2, st));
-    if (rc != CBS_OK) return rc;
-    (void)hipGetLastError();
-    return record_hip(cbs::launch_silu_pass(s, dtype, t2, y, st));
+    if (s.N == 0) return CBS_OK;
+    const uint64_t half = cbs::kNoAllocScratchBytes / 2;
+    const uint64_t ybytes = (uint64_t)s.N * s.C_out * s.OHW * (dtype == CBS_DTYPE_BF16 ? 2 : 4);
+    if (ybytes > half) return CBS_ERR_UNSUPPORTED;  // an intermediate does not fit its half of the scratch
+    if (!h->noalloc_scratch) return record_hip(hipErrorInvalidSymbol);
+    void *t1 = h->noalloc_scratch;
+    void *t2 = (unsigned char *)h->noalloc_scratch + half;
+    return launch_unfused(h, s, dtype, x, w, scale, bias, t1, t2, y, (hipStream_t)stream);
 }
 
 int conv_bn_silu_output_hw(int H, int W, int KH, int KW, int stride, int pad, int *OH, int *OW) {

@@ -63,6 +63,11 @@ bool scalar_supports(const Shape &s, int dtype);
 hipError_t launch_scalar(const Shape &s, int dtype, int epi, const void *x, const void *w,
                          const float *scale, const float *bias, void *y, hipStream_t st);
 
+// Device scratch of the allocation-free unfused entry point: t1 and t2, half
+// each (cbs_noalloc.hip); its address on the current device.
+constexpr uint64_t kNoAllocScratchBytes = 64ull << 20;
+hipError_t noalloc_scratch_address(void **out);
+
 // Element-wise passes of the unfused sequence: t2 = t1*scale[co] + bias[co],
 // then y = SiLU(t2), each rounded to dtype.
 hipError_t launch_bn_pass(const Shape &s, int dtype, const void *t1, const float *scale,

@@ -139,6 +139,27 @@ int conv_bn_silu_run_unfused(conv_bn_silu_t handle,
                              int N, int C_in, int H, int W, int C_out, int KH, int KW,
                              int stride, int pad, int dtype, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * unfused sequence of conv_bn_silu_run_unfused with t1 and t2 held in a
+ * static device array of the library -- 64 MiB per GPU, allocated when the
+ * library is loaded onto that GPU and kept until the process ends -- so the
+ * caller passes only the inputs and y.  Each intermediate (N*C_out*OH*OW
+ * elements of `dtype`) may take at most 32 MiB; larger calls return
+ * CBS_ERR_UNSUPPORTED before touching the device.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine).  Every call on a
+ * GPU uses that GPU's one array: calls that overlap in time on one GPU
+ * (concurrent streams, threads) race on it and must be serialised by the
+ * caller.  Every element of t1 and t2 is written before it is read, so no
+ * clearing is needed between calls.  Validation and status codes as
+ * conv_bn_silu_run; CBS_ERR_HIP if the array's device address could not be
+ * obtained when the handle was created. */
+int conv_bn_silu_run_unfused_noalloc(conv_bn_silu_t handle,
+                                     const void *x, const void *w, const float *scale, const float *bias,
+                                     void *y,
+                                     int N, int C_in, int H, int W, int C_out, int KH, int KW,
+                                     int stride, int pad, int dtype, void *stream);
+
 /* Host-only helpers (no HIP calls, usable without a device). */
 
 /* Output size OH, OW for the given geometry; CBS_ERR_INVALID_ARG if a size
