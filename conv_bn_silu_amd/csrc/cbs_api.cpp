@@ -127,20 +127,24 @@ bool pointers_ok(int variant, const void *x, const void *w, const void *y) {
 }
 
 // AUTO dispatch.  Shape rules in the spirit of the page's hand-picked
-// thresholds ("Three kernels for one operation"): a specialised kernel where
-// the shape fits it, the scalar kernel for tiny problems where any setup
-// costs more than the work, otherwise the generic implicit GEMM.
+// thresholds ("Three kernels for one operation"), set here from measurement
+// on MI355X (bench.py --variants times every variant on shapes on both sides
+// of each rule): the scalar kernel for problems too small for any tiling to
+// pay (up to 2^24 multiply-adds in bf16; in fp32, where the tiled kernel runs
+// on the slower fp32 matrix instructions, up to 2^27), then the specialised
+// kernels where the shape fits them, the 32x32 window kernel for any 3x3
+// layer it serves, the 16x16 window kernel for other filters larger than
+// 1x1, and the generic implicit GEMM otherwise.
 int select(const cbs::Shape &s, int dtype, int num_cu) {
-    (void)num_cu;
+    (void)num_cu;  // the rules are measured on 256 compute units; tiling already adapts to the count
     const int64_t macs = (int64_t)s.M * s.C_out * s.K;
-    if (macs <= (int64_t)1 << 23 && variant_ok(CBS_VARIANT_SCALAR, s, dtype)) return CBS_VARIANT_SCALAR;
+    const int64_t scalar_limit = dtype == CBS_DTYPE_F32 ? (int64_t)1 << 27 : (int64_t)1 << 24;
+    if (macs <= scalar_limit && variant_ok(CBS_VARIANT_SCALAR, s, dtype)) return CBS_VARIANT_SCALAR;
     if (variant_ok(CBS_VARIANT_POINTWISE, s, dtype)) return CBS_VARIANT_POINTWISE;
     if (variant_ok(CBS_VARIANT_SMALL_K, s, dtype)) return CBS_VARIANT_SMALL_K;
     if (variant_ok(CBS_VARIANT_ROWS, s, dtype)) return CBS_VARIANT_ROWS;
-    // Channel-heavy layers whose tiles fill the 32x32 blocks well.
-    if (s.C_in >= 128 && variant_ok(CBS_VARIANT_GEMM_WINDOW32, s, dtype) && cbs::window32_efficiency(s) >= 800)
-        return CBS_VARIANT_GEMM_WINDOW32;
-    if (variant_ok(CBS_VARIANT_GEMM_WINDOW, s, dtype)) return CBS_VARIANT_GEMM_WINDOW;
+    if (variant_ok(CBS_VARIANT_GEMM_WINDOW32, s, dtype)) return CBS_VARIANT_GEMM_WINDOW32;
+    if (s.T > 1 && variant_ok(CBS_VARIANT_GEMM_WINDOW, s, dtype)) return CBS_VARIANT_GEMM_WINDOW;
     return CBS_VARIANT_GEMM_GATHER;
 }
 
