@@ -259,7 +259,7 @@ def mfma_ceiling(num_cu: int, iters: int = 20000) -> dict:
             "mfma_what": f"v_mfma_f32_32x32x16_bf16 on registers, {n_wg} workgroups x 4 waves x {iters} x 8"}
 
 
-def copy_ceiling(num_cu: int, mib: int = 1024, reps: int = 10) -> dict:
+def copy_ceiling(mib: int = 1024, reps: int = 10) -> dict:
     """Our 16-byte streaming copy kernel (k_ceiling.hip) over `mib` MiB:
     read + write bytes per second, the practical ceiling of the streaming
     layers."""
@@ -271,21 +271,20 @@ def copy_ceiling(num_cu: int, mib: int = 1024, reps: int = 10) -> dict:
     b = torch.empty_like(a)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    n_wg = 8 * num_cu
-    for _ in range(2):
-        assert B.lib.conv_bn_silu_bench_copy(a.data_ptr(), b.data_ptr(), n, n_wg, sp) == 0
+    for _ in range(20):
+        assert B.lib.conv_bn_silu_bench_copy(a.data_ptr(), b.data_ptr(), n, sp) == 0
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(reps):
-        assert B.lib.conv_bn_silu_bench_copy(a.data_ptr(), b.data_ptr(), n, n_wg, sp) == 0
+        assert B.lib.conv_bn_silu_bench_copy(a.data_ptr(), b.data_ptr(), n, sp) == 0
     e1.record(stream)
     torch.cuda.synchronize()
     sec = e0.elapsed_time(e1) * 1e-3 / reps
     del a, b
     torch.cuda.empty_cache()
     return {"copy_gbs": round(2 * n / sec / 1e9, 1), "copy_bytes_each_way": n,
-            "copy_what": f"16-byte load/store copy kernel, {n_wg} workgroups of 256"}
+            "copy_what": "copy kernel, one 16-byte load and store per lane, one 256-lane workgroup per 4 KiB"}
 
 
 def cpu_model() -> str:
@@ -473,7 +472,7 @@ def main():
     num_cu = dev.get("num_cu", 256)
     ceil = {}
     if not args.only:
-        ceil.update(copy_ceiling(num_cu))
+        ceil.update(copy_ceiling())
         ceil.update(mfma_ceiling(num_cu))
         log(f"[bench] ceilings: copy {ceil['copy_gbs']:.0f} GB/s, MFMA {ceil['mfma_bf16_tflops']:.0f} TFLOP/s")
 

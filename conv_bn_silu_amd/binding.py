@@ -82,7 +82,7 @@ def _load() -> ctypes.CDLL:
     lib.conv_bn_silu_bench_mfma.restype = i
     lib.conv_bn_silu_bench_mfma_flops.argtypes = [i, i]
     lib.conv_bn_silu_bench_mfma_flops.restype = ctypes.c_int64
-    lib.conv_bn_silu_bench_copy.argtypes = [vp, vp, ctypes.c_uint64, i, vp]
+    lib.conv_bn_silu_bench_copy.argtypes = [vp, vp, ctypes.c_uint64, vp]
     lib.conv_bn_silu_bench_copy.restype = i
     return lib
 

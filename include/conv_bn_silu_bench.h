@@ -31,10 +31,10 @@ int conv_bn_silu_bench_device_info(int *num_cu, int *clock_khz, int *mem_clock_k
 int conv_bn_silu_bench_mfma(int n_wg, int iters, float *sink, void *stream);
 int64_t conv_bn_silu_bench_mfma_flops(int n_wg, int iters);
 
-/* The streaming ceiling: copy `bytes` (a multiple of 16; src and dst 16-byte
- * aligned, not overlapping) with 16-byte loads and stores, n_wg workgroups of
- * 256 lanes. */
-int conv_bn_silu_bench_copy(const void *src, void *dst, uint64_t bytes, int n_wg, void *stream);
+/* The streaming ceiling: copy `bytes` (a multiple of 16, non-zero; src and
+ * dst 16-byte aligned, not overlapping) with one 16-byte load and store per
+ * lane, one workgroup of 256 lanes per 4 KiB. */
+int conv_bn_silu_bench_copy(const void *src, void *dst, uint64_t bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,7 @@ def test_header_and_binding_agree():
 def test_bench_helpers_without_device():
     assert B.lib.conv_bn_silu_bench_mfma_flops(256, 10) == 256 * 4 * 10 * 8 * 2 * 32 * 32 * 16
     assert B.lib.conv_bn_silu_bench_mfma_flops(0, 10) == -1
-    assert B.lib.conv_bn_silu_bench_copy(None, None, 16, 1, None) == 1
+    assert B.lib.conv_bn_silu_bench_copy(None, None, 16, None) == 1
 
 
 @pytest.mark.parametrize("name", declared_functions())
