@@ -25,9 +25,12 @@
 //    distinct bank quarters.
 //  * v_mfma_f32_32x32x16_bf16: per block of 32 channels a wave runs 2 x 7
 //    of them, with the fragment reads issued ahead.
-//  * The epilogue (folded BN, SiLU, bf16 rounding) runs once on the
-//    accumulators and writes 4 consecutive pixels of one channel per lane
-//    (8 bytes); the L2 merges them into whole lines.
+//  * The epilogue (folded BN, SiLU, bf16 rounding) runs on the accumulators
+//    one 32-pixel block at a time: the block is staged in LDS and stored as
+//    16-byte pieces along its 32 channel rows before the next block is
+//    computed, so the stores drain beside the epilogue's arithmetic (measured
+//    1.1 us faster on the 1x1 layer at N=8, 256 -> 256, 80x80 than finishing
+//    every block first).
 #include <type_traits>
 
 #include "cbs_device.h"
@@ -225,13 +228,14 @@ __global__ __launch_bounds__(kThreadsPw, 1) void pointwise_bf16(
     // Epilogue: BN + SiLU on the accumulators (lane: channel co; per block pb
     // and q, pixels 32 pb + 8 q + 4 hi .. +3), bf16, staged in LDS as the
     // wave's [32 channels][L pixels] tile over the weight tile (every wave is
-    // past its last weight read after the barrier), then stored as 16-byte
-    // pieces running along each channel row, so that the writes of a wave
-    // cover whole 2L-byte stretches of 32 planes.
+    // past its last weight read after the barrier); each 32-pixel block is
+    // stored as 16-byte pieces along its channel rows as soon as it is
+    // staged.
     __syncthreads();
     unsigned char *const ot = wsm + wave * 32 * kEpiPitch;
 #pragma unroll
     for (int pb = 0; pb < kMB; ++pb) {
+        if (32 * pb >= len) continue;  // uniform: blocks past a short range
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const float v0 = acc[pb][4 * q], v1 = acc[pb][4 * q + 1];
@@ -246,16 +250,18 @@ __global__ __launch_bounds__(kThreadsPw, 1) void pointwise_bf16(
             }
             *(u32x2 *)(ot + l32 * kEpiPitch + 2 * (32 * pb + 8 * q + 4 * hi)) = o;
         }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's staging writes are done
-    __builtin_amdgcn_wave_barrier();
-    for (int t = lane; t < 32 * qpr; t += 64) {
-        const int r = t / qpr, col = t - r * qpr;
-        int n, p;
-        pix(8 * col, n, p);
-        const int c = ct * kTileCo + wave * 32 + r;
-        const u32x4 v = *(const u32x4 *)(ot + r * kEpiPitch + 16 * col);
-        buf_store16(yr, c < s.C_out ? (uint32_t)((n * s.C_out + c) * hw + p) * 2u : kOOB, v);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's staging writes are done
+        __builtin_amdgcn_wave_barrier();
+        // The block's 32 channel rows x 4 pieces of 8 pixels.
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = lane + 64 * i, r = t >> 2, col = 4 * pb + (t & 3);
+            int n, p;
+            pix(8 * col, n, p);
+            const int c = ct * kTileCo + wave * 32 + r;
+            const u32x4 v = *(const u32x4 *)(ot + r * kEpiPitch + 16 * col);
+            buf_store16(yr, (c < s.C_out && 8 * col < len) ? (uint32_t)((n * s.C_out + c) * hw + p) * 2u : kOOB, v);
+        }
     }
 }
 

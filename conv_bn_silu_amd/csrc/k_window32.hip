@@ -180,7 +180,12 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     // LDS operations run in order, so no barrier is needed for the raw area.
     unsigned char *const raw_w = lds + 2 * kWinBytes + 2 * kWBytes + wave * kRawWave;
     auto w_load = [&](const Blk &b, int q) {
-        const int P = 64 * q + lane, row = P / 18, pc = P - row * 18;
+        // With two staging tasks per thread every register is taken: there
+        // the lane index is produced afresh (volatile asm, not hoisted) so
+        // that no per-lane offset is held across the loops.
+        int ln = lane;
+        if constexpr (TASKS == 2) asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        const int P = 64 * q + ln, row = P / 18, pc = P - row * 18;
         const int co = b.co0 + 32 * wave + row;
         const bool ok = b.live & (co < s.C_out) & (b.ck * kCK32 + (pc >= 9 ? 8 : 0) < s.C_in);
         // the offset is formed for every lane and then selected: left to
@@ -469,10 +474,14 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
         // reciprocal and the lane's own coordinates pass through an empty asm
         // so that every pixel and channel index of the stores is computed
         // here, not hoisted out of the loops into registers the reduction
-        // needs.
+        // needs.  The lane index is recomputed here (mbcnt, in a volatile asm
+        // that cannot be hoisted) rather than kept from the prologue: a value
+        // live across the whole tile loop is one register more than the
+        // two-task staging leaves free.
         int tw_e = g.TW;
         uint32_t rcp_tw = ((1u << 20) + (uint32_t)g.TW - 1) / (uint32_t)g.TW;
-        int lane_e = lane, hf_e = hf;
+        int lane_e, hf_e = hf;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
         asm volatile("" : "+s"(tw_e), "+s"(rcp_tw), "+v"(lane_e), "+s"(hf_e));
         const int l32_e = lane_e & 31, hi_e = lane_e >> 5;
         float sc[2], bi[2];

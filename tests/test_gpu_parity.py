@@ -63,6 +63,10 @@ SWEEP = [
     (5, 256, 8, 8, 16, 1, 1, 1, 0),
     (1, 8, 1, 8, 1, 1, 1, 1, 0),
     (7, 128, 12, 12, 200, 1, 1, 1, 0),
+    # 64-pixel tiles: three channel tiles with a partial last tile, and
+    # 8-pixel images (one tile spans 8 images) with a 200-channel tail
+    (3, 256, 5, 8, 520, 1, 1, 1, 0),
+    (9, 200, 2, 4, 64, 1, 1, 1, 0),
     # enough pixels for full 224-pixel ranges: ranges across image
     # boundaries and a short last range
     (11, 16, 64, 64, 24, 1, 1, 1, 0),
