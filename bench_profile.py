@@ -23,9 +23,20 @@ gpurun_out/).
       operator's kernel and the MFMA work it counted against the layer's
       algorithmic FLOP.
 
+  python3 bench_profile.py stalls  [--workload c5]
+      two counter runs over the bench command: the LDS counters
+      (SQ_INSTS_LDS, SQ_LDS_BANK_CONFLICT, SQ_LDS_ADDR_CONFLICT,
+      SQ_LDS_UNALIGNED_STALL, SQ_LDS_IDX_ACTIVE, SQ_WAIT_INST_LDS,
+      SQ_ACTIVE_INST_LDS), then the wave-time counters (SQ_WAVE_CYCLES,
+      SQ_BUSY_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_ANY,
+      SQ_ACTIVE_INST_VALU, SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA); writes
+      profiles/stalls_<workload>.md with the LDS bank-conflict rate (conflict
+      cycles over LDS active cycles) and the shares of wave time spent
+      waiting and issuing.
+
   python3 bench_profile.py all
-      trace for c1..c5, traffic for c2..c5, mfma for c5: each rocprofv3 pass
-      a run of its own.
+      trace for c1..c5, traffic for c2..c5, mfma for c5, stalls for c2..c5:
+      each rocprofv3 pass a run of its own.
 
 This process never touches the GPU itself: rocprofv3 starts bench.py as a
 child.
@@ -248,9 +259,62 @@ def do_mfma(args) -> None:
     print(f"[profile] wrote {dst}: {json.dumps(rec)}", flush=True)
 
 
+STALL_PASSES = (
+    ["SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT", "SQ_LDS_UNALIGNED_STALL", "SQ_LDS_IDX_ACTIVE",
+     "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS"],
+    ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+     "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA"],
+)
+
+
+def do_stalls(args) -> None:
+    from conv_bn_silu_amd import synth
+    wl = synth.WORKLOADS[args.workload]
+    vals, cmds, variant = {}, [], None
+    for i, counters in enumerate(STALL_PASSES):
+        out = os.path.join(RAW, f"{args.workload}_stalls{i}")
+        c = ["rocprofv3", "--pmc"] + counters + ["--output-format", "csv", "-d", out, "-o", "run", "--"] + \
+            bench_cmd(args.workload, 20)
+        variant = last_json(run(c, 60))["config"]["variant"]
+        cmds.append(" ".join(["timeout -s KILL 60"] + c).replace(out, f"gpurun_out/rocprof/{args.workload}_stalls{i}"))
+        path = os.path.join(out, "run_counter_collection.csv")
+        for ctr in counters:
+            by = counter_by_kernel(path, ctr, lambda k: "cbs" in k)
+            name = max(by, key=lambda n: sum(by[n]))
+            vals[ctr] = mean(by[name])
+            vals["_kernel"] = name[:100]
+    def ratio(a, b):
+        return round(vals[a] / vals[b], 4) if vals.get(b) else None
+    rec = {"workload": wl.name, "variant": variant, "kernel": vals.pop("_kernel"),
+           "counters_per_dispatch": {k: vals[k] for k in vals},
+           "lds_bank_conflict_over_lds_active": ratio("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"),
+           "lds_bank_conflict_cycles_per_lds_instruction": ratio("SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS"),
+           "wave_wait_share": ratio("SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+           "wave_wait_inst_share": ratio("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+           "wave_issue_share": ratio("SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES"),
+           "wave_lds_wait_share": ratio("SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"),
+           "kernel_sources_digest": __import__("bench").kernel_sources_digest(variant)}
+    text = [f"# LDS conflicts and wave stalls: fused conv+BN+SiLU, workload {wl.name}", "",
+            "Two counter runs, each on its own (from the repository root, on one MI355X):", "", "```"] + cmds + \
+           ["```", "",
+            "Per-dispatch means for the operator's kernel, SQ counters summed over the chip.  "
+            "lds_bank_conflict_over_lds_active = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (the share of the LDS "
+            "unit's active cycles lost to bank conflicts); the wave shares divide by SQ_WAVE_CYCLES (the summed "
+            "lifetime of the kernel's waves): SQ_WAIT_ANY counts cycles a wave waits for anything (a dependency, "
+            "a counter, a barrier), SQ_WAIT_INST_ANY cycles it waits to issue its next instruction, "
+            "SQ_ACTIVE_INST_ANY cycles in which it issues one, SQ_WAIT_INST_LDS cycles waiting to issue an LDS "
+            "instruction.", "",
+            "```json", json.dumps(rec, indent=1), "```", ""]
+    os.makedirs(args.out, exist_ok=True)
+    dst = os.path.join(args.out, f"stalls_{wl.name}.md")
+    with open(dst, "w") as f:
+        f.write("\n".join(text))
+    print(f"[profile] wrote {dst}: {json.dumps(rec)}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("mode", choices=["trace", "traffic", "mfma", "all"])
+    ap.add_argument("mode", choices=["trace", "traffic", "mfma", "stalls", "all"])
     ap.add_argument("--workload", default="c5")
     ap.add_argument("--out", default=PROFILES, help="where the summaries go (default profiles/)")
     args = ap.parse_args()
@@ -261,6 +325,8 @@ def main():
         do_mfma(args)
     elif args.mode == "traffic":
         do_traffic(args)
+    elif args.mode == "stalls":
+        do_stalls(args)
     else:
         for key in ("c1", "c2", "c3", "c4", "c5"):
             args.workload = key
@@ -270,6 +336,9 @@ def main():
             do_traffic(args)
         args.workload = "c5"
         do_mfma(args)
+        for key in ("c2", "c3", "c4", "c5"):
+            args.workload = key
+            do_stalls(args)
 
 
 if __name__ == "__main__":

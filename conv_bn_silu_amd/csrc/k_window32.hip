@@ -82,6 +82,17 @@ constexpr int kWinBytes = (160 * 1024 - 2 * kWBytes - 4 * kRawWave) / 2;  // one
 constexpr int kMaxTasks32 = 2;               // window staging tasks per thread, at most
 constexpr int kVec = 8;                      // input columns per window staging load
 
+// Bytes per channel-octet plane of the window: FR rows, padded by one record
+// when the plane's record count is a multiple of 4.  A staging write of 16
+// lanes covers 2 octets x 8 (row, column group) pairs at one column, whose
+// records all fall on 4 residues mod 16 within a plane (the row pitch is
+// fixed by the fragment reads); an octet offset off those residues puts the
+// two octets on distinct banks, halving the conflict.  Fragment reads stay
+// within one plane.
+__host__ __device__ constexpr int win_plane_bytes(int FR, int row_bytes) {
+    return ((FR * row_bytes) >> 4) % 4 == 0 ? FR * row_bytes + 16 : FR * row_bytes;
+}
+
 // Calls f(integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F &&f) {
@@ -138,7 +149,7 @@ __global__ __launch_bounds__(kThreads32, 1) void window32_bf16(
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)s.C_out * s.K * 2u);
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)s.N * s.C_out * s.OHW * 2u);
     const int R = g.row_bytes >> 4;                // window row pitch in records
-    const int plane_bytes = g.FR * g.row_bytes;    // one channel octet of the window
+    const int plane_bytes = win_plane_bytes(g.FR, g.row_bytes);  // one channel octet of the window
 
     // A step: one 16-channel chunk of one tile.
     struct Blk {
@@ -535,7 +546,7 @@ bool make_geo32(const Shape &s, int TH, int TW, int vec, int num_cu, WinGeo *g) 
     int R = g->FCP;
     while ((s.stride * R - TW) % 16 != 0) ++R;
     g->row_bytes = R * 16;
-    if ((int64_t)2 * g->FR * g->row_bytes > kWinBytes) return false;
+    if ((int64_t)2 * win_plane_bytes(g->FR, g->row_bytes) > kWinBytes) return false;
     g->ncg = (g->FC - 1 + vec - 1) / vec + 1;
     // the next chunk's window is staged by at most kTasks32 tasks per thread
     if (2 * g->FR * g->ncg > kMaxTasks32 * kThreads32) return false;
