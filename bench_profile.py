@@ -34,9 +34,23 @@ gpurun_out/).
       cycles over LDS active cycles) and the shares of wave time spent
       waiting and issuing.
 
+  python3 bench_profile.py lds
+      one counter run (SQ_INSTS_LDS, SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE)
+      over the library's LDS probe (conv_bn_silu_bench_lds), one dispatch per
+      address pattern: the bank model's test patterns and the fragment-read
+      and staging patterns of the operator's kernels; writes
+      profiles/lds_bank_model.md.
+
+  python3 bench_profile.py isa
+      times the library's instruction-issue probe (conv_bn_silu_bench_isa)
+      with HIP events in a child process: cycles per wave instruction of
+      fma, exp2, reciprocal, the BN + SiLU epilogue, and of MFMA with
+      independent fmas among them, at 1, 2 and 4 waves per SIMD; writes
+      profiles/isa_rates.md.
+
   python3 bench_profile.py all
-      trace for c1..c5, traffic for c2..c5, mfma for c5, stalls for c2..c5:
-      each rocprofv3 pass a run of its own.
+      trace for c1..c5, traffic for c2..c5, mfma for c5, stalls for c2..c5,
+      lds, isa: each rocprofv3 pass a run of its own.
 
 This process never touches the GPU itself: rocprofv3 starts bench.py as a
 child.
@@ -312,9 +326,198 @@ def do_stalls(args) -> None:
     print(f"[profile] wrote {dst}: {json.dumps(rec)}", flush=True)
 
 
+def lds_cases() -> list[tuple[str, int, list[int]]]:
+    """(name, op, 64 byte addresses): op 0 ds_read_b128, 1 ds_read_b64,
+    2 ds_read_b64_tr_b16, 3 ds_write_b64, 4 ds_write_b128."""
+    lanes = range(64)
+
+    def tr32(pitch):  # 32x32x16 A fragment: 16-lane group g: pixels 16(g&1).., k half g>>1
+        return [(8 * ((l >> 4) >> 1) + ((l & 15) >> 2)) * pitch + 2 * (16 * ((l >> 4) & 1) + 4 * (l & 3))
+                for l in lanes]
+
+    def tr16(pitch, swap=False):  # 16x16x32 A fragment: group g reads rows 8g + (j>>2)
+        out = []
+        for l in lanes:
+            r = 8 * (l >> 4) + ((l & 15) >> 2)
+            pb = 8 * (l & 3)
+            if swap:
+                pb ^= ((r >> 1) & 1) << 6
+            out.append(r * pitch + pb)
+        return out
+
+    def stem(P=672, SLOT=6112):  # 27 (channel, tap row, tap column) arrays, plain pitch
+        out = []
+        for l in lanes:
+            k = 8 * (l >> 4) + ((l & 15) >> 2)
+            ci, r = divmod(k, 9)
+            kh, kw = divmod(r, 3)
+            out.append(kh * SLOT + (3 * ci + kw) * P + 8 * (l & 3))
+        return out
+
+    def win_write(plane):  # window32 staging write at one column, 20x20 tile, row pitch 36 records
+        return [(l & 1) * plane + (((l >> 1) // 4) * 36 + 8 * ((l >> 1) % 4)) * 16 for l in lanes]
+
+    return [
+        ("b128 read, contiguous", 0, [16 * l for l in lanes]),
+        ("b128 read, 16-lane groups contiguous (256 B), 1 KiB apart", 0, [16 * (l % 16) + 1024 * (l // 16) for l in lanes]),
+        ("b128 read, 8-lane groups contiguous (128 B), 512 B apart", 0, [16 * (l % 8) + 512 * (l // 8) for l in lanes]),
+        ("b128 read, stride 256 B", 0, [256 * l for l in lanes]),
+        ("b128 read, one address", 0, [0 for l in lanes]),
+        ("b64 read, contiguous", 1, [8 * l for l in lanes]),
+        ("b64 read, 32-lane halves contiguous (256 B), 1 KiB apart", 1, [8 * (l % 32) + 1024 * (l // 32) for l in lanes]),
+        ("b64 read, 16-lane groups contiguous (128 B), 1 KiB apart", 1, [8 * (l % 16) + 1024 * (l // 16) for l in lanes]),
+        ("tr read, contiguous", 2, [8 * l for l in lanes]),
+        ("tr read, 16-lane groups contiguous (128 B), 1 KiB apart", 2, [8 * (l % 16) + 1024 * (l // 16) for l in lanes]),
+        ("tr read 32x32x16 fragment, row pitch 448 (pointwise)", 2, tr32(448)),
+        ("tr read 32x32x16 fragment, row pitch 320 (strided_rows, OW 160)", 2, tr32(320)),
+        ("tr read 32x32x16 fragment, row pitch 512", 2, tr32(512)),
+        ("tr read 16x16x32 fragment, row pitch 128", 2, tr16(128)),
+        ("tr read 16x16x32 fragment, row pitch 128, halves swapped on row bit 1", 2, tr16(128, True)),
+        ("tr read 16x16x32 fragment, row pitch 192", 2, tr16(192)),
+        ("tr read 16x16x32 fragment, stem arrays (672 B pitch, 6112 B rows)", 2, stem()),
+        ("b64 write, contiguous", 3, [8 * l for l in lanes]),
+        ("b128 write, contiguous", 4, [16 * l for l in lanes]),
+        ("b128 write, window32 staging, octet planes 12672 B apart (792 records)", 4, win_write(12672)),
+        ("b128 write, window32 staging, octet planes 12688 B apart (793 records)", 4, win_write(12688)),
+    ]
+
+
+def lds_child(path: str) -> None:
+    """Child of the `lds` mode: one probe dispatch per case, in order."""
+    import torch
+    from conv_bn_silu_amd import binding as B
+    out = torch.zeros(64, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    cases = lds_cases()
+    for name, op, addrs in cases:
+        assert len(addrs) == 64 and all(0 <= a < 65536 - 16 for a in addrs), name
+        a = torch.tensor(addrs, dtype=torch.int32, device="cuda")
+        if B.lib.conv_bn_silu_bench_lds(op, a.data_ptr(), out.data_ptr(), st) != 0:
+            raise SystemExit(f"probe launch failed: {name}")
+        torch.cuda.synchronize()
+    with open(path, "w") as f:
+        json.dump([c[0] for c in cases], f)
+    print(json.dumps({"cases": len(cases)}), flush=True)
+
+
+def do_lds(args) -> None:
+    out = os.path.join(RAW, "lds_probe")
+    names_path = os.path.join(out, "cases.json")
+    os.makedirs(out, exist_ok=True)
+    counters = ["SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"]
+    c = ["rocprofv3", "--pmc"] + counters + ["--output-format", "csv", "-d", out, "-o", "run", "--",
+                                             "python3", "bench_profile.py", "lds-child", "--cases", names_path]
+    run(c, 90)
+    names = json.load(open(names_path))
+    per = {}
+    for r in read_csv(os.path.join(out, "run_counter_collection.csv")):
+        if "lds_probe" not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(per)
+    if len(ids) != len(names):
+        raise SystemExit(f"{len(ids)} probe dispatches for {len(names)} cases")
+    # 64 conflict-free 16-byte initial stores per lane precede the 256 probed
+    # operations; per probed operation: (counter - init) / 256.
+    init = per[ids[names.index("b128 write, contiguous")]]
+    init_active = init["SQ_LDS_IDX_ACTIVE"] / 5.0  # 64 of the 320 writes there, each 8 cycles (see below)
+    rows = []
+    for i, name in zip(ids, names):
+        d = per[i]
+        conf = d["SQ_LDS_BANK_CONFLICT"] / 256.0
+        active = (d["SQ_LDS_IDX_ACTIVE"] - init_active) / 256.0
+        rows.append((name, round(conf, 2), round(active, 2)))
+    text = ["# LDS bank model: measured per address pattern", "",
+            "One counter run (from the repository root, on one MI355X):", "", "```",
+            " ".join(["timeout -s KILL 90"] + c).replace(out, "gpurun_out/rocprof/lds_probe"), "```", "",
+            "Each case is one dispatch of the library's LDS probe (`conv_bn_silu_bench_lds`): one wave repeats one "
+            "LDS operation 256 times at the per-lane addresses the case lists (`lds_cases()` in "
+            "bench_profile.py), after 64 conflict-free 16-byte stores per lane that fill the array.  Per probed "
+            "operation: bank-conflict cycles (SQ_LDS_BANK_CONFLICT / 256) and LDS active cycles "
+            "(SQ_LDS_IDX_ACTIVE less the initial stores, / 256).", "",
+            "| pattern | conflict cycles per op | LDS cycles per op |", "|---|---|---|"]
+    text += [f"| {n} | {cf} | {ac} |" for n, cf, ac in rows]
+    text += ["", "Reading: 16-byte operations are served 16 lanes (256 bytes) per LDS cycle, 8-byte ones and the "
+             "transposed read 32 lanes per cycle; a pass is conflict-free when its lanes cover 256 distinct "
+             "bytes (one repeated address is broadcast).", ""]
+    os.makedirs(args.out, exist_ok=True)
+    dst = os.path.join(args.out, "lds_bank_model.md")
+    with open(dst, "w") as f:
+        f.write("\n".join(text))
+    print(f"[profile] wrote {dst}", flush=True)
+
+
+ISA_KINDS = [(0, "v_fma_f32", 1), (1, "v_exp_f32", 1), (2, "v_add_f32 + v_rcp_f32", 2),
+             (3, "BN + SiLU epilogue (2 fma, exp, add, rcp, mul)", 6)]
+MFMA_KINDS = [(10, 0), (11, 8), (12, 16), (14, 32), (18, 64)]
+
+
+def isa_child() -> None:
+    """Child of the `isa` mode: times the issue probes with HIP events."""
+    import torch
+    from conv_bn_silu_amd import binding as B
+    st = torch.cuda.current_stream()
+    num_cu = 256
+    sink = torch.empty(4 * num_cu * 256, device="cuda")
+
+    def timed(kind, n_wg, iters):
+        for _ in range(3):
+            if B.lib.conv_bn_silu_bench_isa(kind, n_wg, iters, sink.data_ptr(), st.cuda_stream) != 0:
+                raise SystemExit(f"probe launch failed: kind {kind}")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(5):
+            B.lib.conv_bn_silu_bench_isa(kind, n_wg, iters, sink.data_ptr(), st.cuda_stream)
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / 5
+
+    clock = 2.4e9
+    rec = {"clock_hz_assumed": clock, "vector": [], "mfma": []}
+    for kind, what, n_instr in ISA_KINDS:
+        for wps in (1, 2, 4):
+            s = timed(kind, num_cu * wps, 20000)
+            per = s * clock / (wps * 20000 * 8)  # cycles per 8-chain step of one wave, per SIMD
+            rec["vector"].append({"what": what, "waves_per_simd": wps, "seconds": s,
+                                  "cycles_per_element_group": round(per, 2),
+                                  "cycles_per_instruction": round(per / n_instr, 2)})
+    for kind, nv in MFMA_KINDS:
+        for wps in (1, 2):
+            s = timed(kind, num_cu * wps, 5000)
+            rec["mfma"].append({"fmas_per_8_mfma": nv, "waves_per_simd": wps, "seconds": s,
+                                "cycles_per_mfma": round(s * clock / (wps * 5000 * 8), 2)})
+    print(json.dumps(rec), flush=True)
+
+
+def do_isa(args) -> None:
+    cmd = ["python3", "bench_profile.py", "isa-child"]
+    rec = last_json(run(cmd, 300))
+    text = ["# Instruction issue rates: measured", "", "Command (from the repository root, on one MI355X):", "",
+            "```", "timeout -s KILL 300 " + " ".join(cmd), "```", "",
+            "The library's issue probe (`conv_bn_silu_bench_isa`), 256, 512 or 1024 workgroups of 4 waves (1, 2, "
+            "4 waves per SIMD), 8 independent chains per lane, register-only; HIP events around 5 launches.  "
+            "Cycles at an assumed 2.4 GHz, per SIMD: for the vector kinds per 64-lane step of one chain "
+            "(and per instruction of it), for the matrix kinds per v_mfma_f32_32x32x16_bf16 with the given "
+            "number of independent v_fma_f32 per 8 of them.", "",
+            "| vector work | waves/SIMD | cycles per 64 elements | per instruction |", "|---|---|---|---|"]
+    text += [f"| {r['what']} | {r['waves_per_simd']} | {r['cycles_per_element_group']} | {r['cycles_per_instruction']} |"
+             for r in rec["vector"]]
+    text += ["", "| fmas per 8 MFMA | waves/SIMD | cycles per MFMA |", "|---|---|---|"]
+    text += [f"| {r['fmas_per_8_mfma']} | {r['waves_per_simd']} | {r['cycles_per_mfma']} |" for r in rec["mfma"]]
+    text += ["", "```json", json.dumps(rec, indent=1), "```", ""]
+    os.makedirs(args.out, exist_ok=True)
+    dst = os.path.join(args.out, "isa_rates.md")
+    with open(dst, "w") as f:
+        f.write("\n".join(text))
+    print(f"[profile] wrote {dst}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("mode", choices=["trace", "traffic", "mfma", "stalls", "all"])
+    ap.add_argument("mode", choices=["trace", "traffic", "mfma", "stalls", "lds", "isa", "all", "lds-child", "isa-child"])
+    ap.add_argument("--cases", default="", help=argparse.SUPPRESS)
     ap.add_argument("--workload", default="c5")
     ap.add_argument("--out", default=PROFILES, help="where the summaries go (default profiles/)")
     args = ap.parse_args()
@@ -327,6 +530,14 @@ def main():
         do_traffic(args)
     elif args.mode == "stalls":
         do_stalls(args)
+    elif args.mode == "lds":
+        do_lds(args)
+    elif args.mode == "isa":
+        do_isa(args)
+    elif args.mode == "lds-child":
+        lds_child(args.cases)
+    elif args.mode == "isa-child":
+        isa_child()
     else:
         for key in ("c1", "c2", "c3", "c4", "c5"):
             args.workload = key
@@ -339,6 +550,8 @@ def main():
         for key in ("c2", "c3", "c4", "c5"):
             args.workload = key
             do_stalls(args)
+        do_lds(args)
+        do_isa(args)
 
 
 if __name__ == "__main__":

@@ -36,7 +36,7 @@ EXPORTS = [
 # Measurement support (include/conv_bn_silu_bench.h).
 BENCH_EXPORTS = [
     "conv_bn_silu_bench_device_info", "conv_bn_silu_bench_mfma", "conv_bn_silu_bench_mfma_flops",
-    "conv_bn_silu_bench_copy",
+    "conv_bn_silu_bench_copy", "conv_bn_silu_bench_lds", "conv_bn_silu_bench_isa",
 ]
 
 
@@ -84,6 +84,10 @@ def _load() -> ctypes.CDLL:
     lib.conv_bn_silu_bench_mfma_flops.restype = ctypes.c_int64
     lib.conv_bn_silu_bench_copy.argtypes = [vp, vp, ctypes.c_uint64, vp]
     lib.conv_bn_silu_bench_copy.restype = i
+    lib.conv_bn_silu_bench_lds.argtypes = [i, vp, vp, vp]
+    lib.conv_bn_silu_bench_lds.restype = i
+    lib.conv_bn_silu_bench_isa.argtypes = [i, i, i, vp, vp]
+    lib.conv_bn_silu_bench_isa.restype = i
     return lib
 
 
