@@ -39,6 +39,14 @@ def test_bench_helpers_without_device():
     assert B.lib.conv_bn_silu_bench_mfma_flops(256, 10) == 256 * 4 * 10 * 8 * 2 * 32 * 32 * 16
     assert B.lib.conv_bn_silu_bench_mfma_flops(0, 10) == -1
     assert B.lib.conv_bn_silu_bench_copy(None, None, 16, None) == 1
+    # the probes reject bad arguments before touching a device
+    assert B.lib.conv_bn_silu_bench_lds(0, None, None, None) == 1
+    assert B.lib.conv_bn_silu_bench_lds(5, 16, 16, None) == 1
+    assert B.lib.conv_bn_silu_bench_lds(-1, 16, 16, None) == 1
+    assert B.lib.conv_bn_silu_bench_isa(0, 256, 10, None, None) == 1
+    assert B.lib.conv_bn_silu_bench_isa(7, 256, 10, 16, None) == 1
+    assert B.lib.conv_bn_silu_bench_isa(0, 0, 10, 16, None) == 1
+    assert B.lib.conv_bn_silu_bench_isa(0, 256, 0, 16, None) == 1
 
 
 @pytest.mark.parametrize("name", declared_functions())

@@ -100,3 +100,16 @@ def test_dispatch_sweep_shapes_are_valid():
     from conv_bn_silu_amd import binding as B
     for g in bench.DISPATCH_SWEEP:
         assert B.select_variant(*g[:10]) in range(1, 8), g
+
+
+def test_lds_probe_cases_fit_the_probe():
+    """Every LDS-probe address pattern stays inside the probe's 64 KiB array,
+    is aligned for its operation and names one of the five operations."""
+    import bench_profile as bp
+    cases = bp.lds_cases()
+    assert len({n for n, _, _ in cases}) == len(cases)
+    for name, op, addrs in cases:
+        assert op in (0, 1, 2, 3, 4), name
+        assert len(addrs) == 64, name
+        align = 16 if op in (0, 4) else 8
+        assert all(0 <= a < 65536 - 16 and a % align == 0 for a in addrs), name
