@@ -48,9 +48,15 @@ gpurun_out/).
       independent fmas among them, at 1, 2 and 4 waves per SIMD; writes
       profiles/isa_rates.md.
 
+  python3 bench_profile.py resources
+      (no GPU) the compiler's per-kernel resource report that
+      conv_bn_silu_amd/build.py writes beside the library (registers,
+      scratch, LDS, waves per SIMD), demangled, as
+      profiles/kernel_resources.md.
+
   python3 bench_profile.py all
       trace for c1..c5, traffic for c2..c5, mfma for c5, stalls for c2..c5,
-      lds, isa: each rocprofv3 pass a run of its own.
+      lds, isa, resources: each rocprofv3 pass a run of its own.
 
 This process never touches the GPU itself: rocprofv3 starts bench.py as a
 child.
@@ -514,9 +520,34 @@ def do_isa(args) -> None:
     print(f"[profile] wrote {dst}", flush=True)
 
 
+def do_resources(args) -> None:
+    src = os.path.join(ROOT, "conv_bn_silu_amd", "libconv_bn_silu.resources.txt")
+    if not os.path.exists(src):
+        raise SystemExit("no resource report: run python3 conv_bn_silu_amd/build.py first")
+    rows = [l.split() for l in open(src) if l.strip() and not l.startswith("#")]
+    filt = "c++filt"
+    names = subprocess.run([filt], input="\n".join(r[0] for r in rows), capture_output=True, text=True,
+                           check=True).stdout.splitlines()
+    text = ["# Kernel resources (compiler report)", "", "Command (from the repository root, no GPU needed):", "",
+            "```", "python3 conv_bn_silu_amd/build.py && python3 bench_profile.py resources", "```", "",
+            "Per kernel instantiation, from hipcc's `-Rpass-analysis=kernel-resource-usage` remarks for gfx950 "
+            "(the build fails if any kernel needs scratch): VGPRs, AGPRs, scratch bytes per lane, LDS bytes "
+            "per workgroup, waves per SIMD the registers and LDS allow.", "",
+            "| kernel | VGPR | AGPR | scratch | LDS | waves/SIMD |", "|---|---|---|---|---|---|"]
+    for r, n in zip(rows, names):
+        short = n.replace("cbs::(anonymous namespace)::", "").split("(")[0]
+        text.append(f"| `{short}` | {r[1]} | {r[2]} | {r[3]} | {r[4]} | {r[5]} |")
+    os.makedirs(args.out, exist_ok=True)
+    dst = os.path.join(args.out, "kernel_resources.md")
+    with open(dst, "w") as f:
+        f.write("\n".join(text) + "\n")
+    print(f"[profile] wrote {dst}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("mode", choices=["trace", "traffic", "mfma", "stalls", "lds", "isa", "all", "lds-child", "isa-child"])
+    ap.add_argument("mode", choices=["trace", "traffic", "mfma", "stalls", "lds", "isa", "resources", "all", "lds-child",
+                                         "isa-child"])
     ap.add_argument("--cases", default="", help=argparse.SUPPRESS)
     ap.add_argument("--workload", default="c5")
     ap.add_argument("--out", default=PROFILES, help="where the summaries go (default profiles/)")
@@ -534,6 +565,8 @@ def main():
         do_lds(args)
     elif args.mode == "isa":
         do_isa(args)
+    elif args.mode == "resources":
+        do_resources(args)
     elif args.mode == "lds-child":
         lds_child(args.cases)
     elif args.mode == "isa-child":
@@ -552,6 +585,7 @@ def main():
             do_stalls(args)
         do_lds(args)
         do_isa(args)
+        do_resources(args)
 
 
 if __name__ == "__main__":
