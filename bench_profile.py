@@ -54,6 +54,13 @@ gpurun_out/).
       scratch, LDS, waves per SIMD), demangled, as
       profiles/kernel_resources.md.
 
+  python3 bench_profile.py dispatch
+      bench.py --variants --no-cpu-baseline in a child: every variant that
+      supports each of the five workloads and of the dispatch sweep's
+      shapes, timed, against AUTO's pick; writes profiles/dispatch_sweep.md
+      (exits non-zero, as bench.py does, when AUTO is more than 5% slower
+      than the fastest variant anywhere).
+
   python3 bench_profile.py all
       trace for c1..c5, traffic for c2..c5, mfma for c5, stalls for c2..c5,
       lds, isa, resources: each rocprofv3 pass a run of its own.
@@ -544,9 +551,39 @@ def do_resources(args) -> None:
     print(f"[profile] wrote {dst}", flush=True)
 
 
+def do_dispatch(args) -> None:
+    cmd = ["python3", "bench.py", "--variants", "--no-cpu-baseline"]
+    print("[profile] " + " ".join(cmd), flush=True)
+    p = subprocess.run(["timeout", "-s", "KILL", "900"] + cmd, cwd=ROOT, stdout=subprocess.PIPE, text=True)
+    if p.returncode not in (0, 3):
+        raise SystemExit(f"bench.py failed with status {p.returncode}")
+    d = last_json(p.stdout)["dispatch"]
+    text = ["# Dispatch check: AUTO against every variant, fused conv+BN+SiLU", "",
+            "Command (from the repository root, on one MI355X):", "", "```", " ".join(cmd), "```", "",
+            "Every variant that supports each shape, timed (kernel microseconds per launch, HIP events over the "
+            "timed region, after a short untimed settle); the five workloads first, then shapes on both sides of "
+            "each dispatch rule (bench.py DISPATCH_SWEEP).  bench.py exits with status 3 when AUTO's pick is more "
+            "than 5% slower than the fastest variant on any shape.", "",
+            "| shape | N x C_in x H x W -> C_out, filter | variants (us, fastest first) | AUTO picks | AUTO / fastest |",
+            "|---|---|---|---|---|"]
+    for c in d["shapes"]:
+        N, C_in, H, W, C_out, KH, KW, st, pad, dt = c["shape"]
+        var = ", ".join(f"{k} {v:.1f}" for k, v in sorted(c["variants_us"].items(), key=lambda kv: kv[1]))
+        text.append(f"| {c['name']} | {N}x{C_in}x{H}x{W} -> {C_out}, {KH}x{KW} s{st} p{pad}, "
+                    f"{'bf16' if dt else 'fp32'} | {var} | {c['auto_picks']} | {c['auto_over_fastest']} |")
+    text += ["", f"Worst AUTO / fastest: {d['worst_auto_over_fastest']} (within 5%: {d['auto_within_5pct']}).", ""]
+    os.makedirs(args.out, exist_ok=True)
+    dst = os.path.join(args.out, "dispatch_sweep.md")
+    with open(dst, "w") as f:
+        f.write("\n".join(text))
+    print(f"[profile] wrote {dst}", flush=True)
+    if not d["auto_within_5pct"]:
+        raise SystemExit(3)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("mode", choices=["trace", "traffic", "mfma", "stalls", "lds", "isa", "resources", "all", "lds-child",
+    ap.add_argument("mode", choices=["trace", "traffic", "mfma", "stalls", "lds", "isa", "resources", "dispatch", "all", "lds-child",
                                          "isa-child"])
     ap.add_argument("--cases", default="", help=argparse.SUPPRESS)
     ap.add_argument("--workload", default="c5")
@@ -567,6 +604,8 @@ def main():
         do_isa(args)
     elif args.mode == "resources":
         do_resources(args)
+    elif args.mode == "dispatch":
+        do_dispatch(args)
     elif args.mode == "lds-child":
         lds_child(args.cases)
     elif args.mode == "isa-child":
