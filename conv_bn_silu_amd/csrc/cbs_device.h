@@ -69,6 +69,15 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t of
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
 }
+// As buf_store16 with the non-temporal (streaming) cache policy.  Measured on
+// gfx950: where every store instruction writes whole aligned 64-byte
+// segments (four consecutive lanes per segment), y streams out during the
+// kernel and the layer runs faster; where a segment is split between
+// instructions, or a lane writes 8 bytes, it is markedly slower, so callers
+// use it only for whole-segment store patterns.
+__device__ __forceinline__ void buf_store16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 2);
+}
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
