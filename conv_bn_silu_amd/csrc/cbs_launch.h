@@ -58,7 +58,7 @@ int window32_efficiency(const Shape &s);
 hipError_t launch_window32(const Shape &s, int epi, const void *x, const void *w, const float *scale,
                            const float *bias, void *y, hipStream_t st, int num_cu);
 
-// One output element per lane; any geometry, both dtypes.
+// Each lane computes a single output; any geometry, both dtypes.
 bool scalar_supports(const Shape &s, int dtype);
 hipError_t launch_scalar(const Shape &s, int dtype, int epi, const void *x, const void *w,
                          const float *scale, const float *bias, void *y, hipStream_t st);

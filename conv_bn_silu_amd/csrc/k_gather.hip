@@ -6,7 +6,8 @@
 // No im2col matrix is materialised: every 32-wide k slice of the pixel
 // operand is gathered straight from NCHW x into LDS (zeros for padding and for
 // the ragged K and M tails), the weight slice is copied from OIHW w, and the
-// K loop is the tiled "acc += A_tile @ B_tile" of section "The shape of it".
+// K loop accumulates one tile product per k slice, as in the tiled loop of
+// section "The shape of it".
 // After the loop the tile is still in registers and the epilogue applies the
 // folded batch norm and SiLU before the single store.
 //

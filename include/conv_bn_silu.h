@@ -58,8 +58,8 @@ enum {
 enum { CBS_DTYPE_F32 = 0, CBS_DTYPE_BF16 = 1 };
 
 /* Kernel variants.  AUTO lets the library choose from the shape (the page's
- * "Three kernels for one operation": several implementations of the same
- * fused operation, picked by shape).  The others force one implementation;
+ * section "Three kernels for one operation": one operator, several kernels,
+ * the kernel chosen per shape).  The others force one implementation;
  * they exist so that tests and benchmarks can check each variant on every
  * shape it may serve. */
 enum {
@@ -72,7 +72,7 @@ enum {
     CBS_VARIANT_SMALL_K = 4,     /* small reduction: the 3x3 stride-2 pad-1 RGB stem
                                     (C_in <= 3, C_out <= 16, W a multiple of 32,
                                     OW <= 320), K = 27 in one MFMA step (bf16) */
-    CBS_VARIANT_SCALAR = 5,      /* one output element per lane, no tiling; small shapes */
+    CBS_VARIANT_SCALAR = 5,      /* each lane computes a single output, no tiling; small shapes */
     CBS_VARIANT_GEMM_WINDOW32 = 6, /* as GEMM_WINDOW on 32x32x16 MFMA with larger tiles
                                       per wave: channel-heavy layers (bf16) */
     CBS_VARIANT_ROWS = 7,        /* 3x3 stride-2 pad-1 layers with C_in a multiple of 16
