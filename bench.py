@@ -188,6 +188,58 @@ def measure_fused(wl, steps: int, warmup: int, variant: str = "auto", layer: Lay
             "hbm_gbs_alg": wl.algorithmic_bytes / kern / 1e9}
 
 
+GRAPH_SETS = 32
+
+
+def measure_graph(wl, reps: int = 20, layer: Layer | None = None) -> dict:
+    """The fused call on up to GRAPH_SETS buffer sets captured once in a HIP
+    graph (torch.cuda.CUDAGraph) and the graph replayed `reps` times between
+    a HIP event pair: the time per launch without the host issuing each
+    launch (which bounds the smallest layer when launches are issued one at
+    a time).  Returns {"us_per_launch": None, "error": ...} if capture fails."""
+    import torch
+    from conv_bn_silu_amd import binding as B
+    L = layer or Layer(wl)
+    lib = B.default_library()
+    v = B.select_variant(*L.geo)
+    k = min(L.sets, GRAPH_SETS)
+    fn, handle = B.lib.conv_bn_silu_run_variant, lib.handle
+
+    def calls(sp):
+        for j in range(k):
+            rc = fn(handle, v, L.xs[j].data_ptr(), L.w.data_ptr(), L.sc.data_ptr(), L.bi.data_ptr(),
+                    L.ys[j][0].data_ptr(), *L.geo, sp)
+            if rc:
+                raise RuntimeError(f"conv_bn_silu_run_variant returned {rc}")
+
+    try:
+        cur = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            calls(side.cuda_stream)
+        cur.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls(torch.cuda.current_stream().cuda_stream)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(reps):
+            g.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * k)
+        del g
+        return {"us_per_launch": round(us, 3), "launches_per_graph": k, "replays": reps}
+    except Exception as exc:  # the line is still printed; the failure is reported in it
+        torch.cuda.synchronize()
+        return {"us_per_launch": None, "error": f"{type(exc).__name__}: {exc}"}
+
+
 def measure_unfused(wl, steps: int, warmup: int) -> dict:
     """conv -> t1, BN -> t2, SiLU -> y, the intermediates in HBM."""
     import torch
@@ -506,13 +558,18 @@ def main():
         layers = {}
         for key in sorted(synth.WORKLOADS):
             wlk = synth.WORKLOADS[key]
-            q = r if key == args.workload and args.variant == "auto" else measure_fused(wlk, sub_steps, args.warmup)
+            Lk = None if key == args.workload and args.variant == "auto" else Layer(wlk)
+            q = r if Lk is None else measure_fused(wlk, sub_steps, args.warmup, layer=Lk)
             ent = layer_entry(q, ceil)
+            gr = measure_graph(wlk, layer=Lk)
+            ent["graph_us_per_launch"] = gr["us_per_launch"]
+            if gr.get("error"):
+                ent["graph_error"] = gr["error"]
             u = measure_unfused(wlk, sub_steps, args.warmup)
             ent["unfused_us_per_step"] = round(u["us_per_step"], 3)
             ent["fused_speedup_over_unfused"] = round(u["us_per_step"] / (q["kernel_s"] * 1e6), 3)
             log(f"[bench] layer {key}: {ent['kernel_us']:.2f} us ({ent['variant']}, frac {ent['frac']}), "
-                f"unfused {ent['unfused_us_per_step']:.2f} us")
+                f"graph-replayed {ent['graph_us_per_launch']} us, unfused {ent['unfused_us_per_step']:.2f} us")
             layers[wlk.name] = ent
         out["layers"] = layers
     if args.variants:

@@ -262,6 +262,49 @@ def test_side_stream(lib):
     U.check(U.to_f64(y), U.oracle_full(inp), BF16, "side stream")
 
 
+@pytest.mark.parametrize("key", ["c1", "c2", "c5"])
+def test_graph_capture_replays(lib, key):
+    """The fused call captured in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed four times, with eager work and synchronisations between the
+    replays: every replay writes exactly the eager call's bits, and the
+    eager call matches the oracle.  The call only enqueues kernels (no
+    allocation, no memset), so it can be captured."""
+    import torch
+    wl = synth.WORKLOADS[key]
+    if key != "c1":
+        wl = wl.with_(N=1)
+    inp = synth.make_inputs(wl)
+    x, w, sc, bi = U.upload(inp)
+    U.say(f"[graph] {key} eager")
+    ref = lib.conv_bn_silu(x, w, sc, bi, stride=wl.stride, pad=wl.pad)
+    torch.cuda.synchronize()
+    U.check(U.to_f64(ref), U.oracle_full(inp), wl.dtype, f"{key} eager")
+    bits = torch.int16 if ref.dtype == torch.bfloat16 else torch.int32
+    y = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # a warm-up call off the default stream before capture
+        lib.conv_bn_silu(x, w, sc, bi, stride=wl.stride, pad=wl.pad, out=y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    U.say(f"[graph] {key} capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.conv_bn_silu(x, w, sc, bi, stride=wl.stride, pad=wl.pad, out=y)
+    torch.cuda.synchronize()
+    for r in range(4):
+        y.view(bits).fill_(0x5A5A)  # a replay that wrote nothing would leave this pattern
+        torch.cuda.synchronize()
+        U.say(f"[graph] {key} replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(bits), ref.view(bits)), f"{key}: replay {r} differs from the eager call"
+        z = lib.conv_bn_silu(x, w, sc, bi, stride=wl.stride, pad=wl.pad)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(z.view(bits), ref.view(bits))
+    del g
+
+
 @pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5"])
 def test_unfused_sequence(lib, key):
     """The three-kernel baseline: each pass checked against the oracle's pass
