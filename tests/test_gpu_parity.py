@@ -8,8 +8,9 @@ counts off the tile sizes, M and K tails); the five workloads with a reduced
 batch checked in full; the five workloads at full size, in the launch
 configuration the benchmark times, every output checked; the epilogue's
 special values (SiLU(0) = 0, the closed forms, saturation to -0 and to v) on
-every variant; one handle driving two streams at once; and the degenerate
-cases (empty batch, 1x1x1, padding wider than the window's reach)."""
+every variant; one handle driving two streams at once; the call captured in a
+HIP graph and replayed; and the degenerate cases (empty batch, 1x1x1, padding
+wider than the window's reach)."""
 import numpy as np
 import pytest
 
