@@ -67,7 +67,7 @@ __device__ __forceinline__ void unroll(F &&f) {
 
 constexpr int kStemWaves = 4;
 constexpr int kStemThreads = 64 * kStemWaves;
-constexpr int kStemPD = 2;  // steps of input rows in flight in registers (>= 1)
+constexpr int kStemPD = 3;  // steps of input rows in flight in registers (>= 1; 3 measured fastest)
 constexpr int kRing = 9;    // input-row slots: 3 steps x 3 rows (see the step loop)
 
 // Compile-time geometry for output rows of at most 64*NBW pixels (NBW:
