@@ -23,8 +23,9 @@ Prints ONE JSON line: the metric (TFLOP/s), the roofline of the dominant
 kernel, the HBM traffic counted by rocprofv3 (when the committed counter
 record matches the current kernel source), the measured ceilings (a
 register-only MFMA loop and a streaming copy, both our own kernels), each
-layer's figures with the unfused three-kernel sequence beside it, and the CPU
-oracle timed on a bounded sample on the host cores.
+layer's figures with the unfused three-kernel sequence beside it (and, for
+the HBM-bound layers, the copy kernel moving the same number of bytes), and
+the CPU oracle timed on a bounded sample on the host cores.
 
 Flags:
   --workload KEY  headline layer (default c5)
@@ -336,7 +337,37 @@ def copy_ceiling(mib: int = 1024, reps: int = 10) -> dict:
     del a, b
     torch.cuda.empty_cache()
     return {"copy_gbs": round(2 * n / sec / 1e9, 1), "copy_bytes_each_way": n,
-            "copy_what": "copy kernel, one 16-byte load and store per lane, one 256-lane workgroup per 4 KiB"}
+            "copy_what": "copy kernel, one 16-byte load and store per lane, one 256-lane workgroup per 4 KiB, "
+                         "non-temporal stores"}
+
+
+def same_bytes_copy(wl, reps: int = 100) -> dict:
+    """The copy kernel moving the layer's algorithmic bytes (half read, half
+    written), on rotated buffer pairs as the layer's own timing uses, timed
+    per launch: what a kernel of this size costs when it does nothing but
+    stream its bytes, start-up and tail included."""
+    import torch
+    from conv_bn_silu_amd import binding as B
+    n = (wl.algorithmic_bytes // 2 + 15) // 16 * 16
+    sets = max(2, math.ceil(2 * MALL_BYTES / (2 * n)))
+    src = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    dst = [torch.empty_like(a) for a in src]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    fn = B.lib.conv_bn_silu_bench_copy
+    for i in range(max(20, reps // 2)):
+        assert fn(src[i % sets].data_ptr(), dst[i % sets].data_ptr(), n, sp) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(reps):
+        assert fn(src[i % sets].data_ptr(), dst[i % sets].data_ptr(), n, sp) == 0
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"us": round(us, 3), "bytes_each_way": n, "sets": sets}
 
 
 def cpu_model() -> str:
@@ -565,11 +596,16 @@ def main():
             ent["graph_us_per_launch"] = gr["us_per_launch"]
             if gr.get("error"):
                 ent["graph_error"] = gr["error"]
+            if ent["bound"] == "hbm":
+                cp = same_bytes_copy(wlk)
+                ent["same_bytes_copy_us"] = cp["us"]
+                ent["over_same_bytes_copy"] = round(ent["kernel_us"] / cp["us"], 4)
             u = measure_unfused(wlk, sub_steps, args.warmup)
             ent["unfused_us_per_step"] = round(u["us_per_step"], 3)
             ent["fused_speedup_over_unfused"] = round(u["us_per_step"] / (q["kernel_s"] * 1e6), 3)
             log(f"[bench] layer {key}: {ent['kernel_us']:.2f} us ({ent['variant']}, frac {ent['frac']}), "
-                f"graph-replayed {ent['graph_us_per_launch']} us, unfused {ent['unfused_us_per_step']:.2f} us")
+                f"graph-replayed {ent['graph_us_per_launch']} us, same-bytes copy "
+                f"{ent.get('same_bytes_copy_us', '-')} us, unfused {ent['unfused_us_per_step']:.2f} us")
             layers[wlk.name] = ent
         out["layers"] = layers
     if args.variants:
