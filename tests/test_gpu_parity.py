@@ -94,10 +94,15 @@ SWEEP = [
     (1, 64, 33, 64, 128, 3, 3, 2, 1),
     (3, 32, 20, 320, 136, 3, 3, 2, 1),
     (2, 48, 12, 96, 64, 3, 3, 2, 1),
-    # more output rows than ranks with an odd chunk count: several loop
-    # iterations of two rows each, and a padding row at the end for some ranks
+    # more output rows than ranks: several rows per workgroup with three
+    # chunks (a prefetch depth of three units), and with one chunk (the
+    # producers' loop ends in a partial round of units)
     (6, 48, 200, 32, 64, 3, 3, 2, 1),
     (5, 16, 240, 16, 24, 3, 3, 2, 1),
+    # widest row class with OW not a multiple of 8 (8-byte output pieces;
+    # with one or two chunks a prefetch depth of two units)
+    (1, 32, 10, 296, 64, 3, 3, 2, 1),
+    (2, 16, 6, 296, 40, 3, 3, 2, 1),
     # 32x32 window variant: more tiles than compute units (two tiles per
     # workgroup: the tile loop and the next tile's BN factors), an odd chunk
     # count (a padding chunk), a partial last channel tile, stride 2 with
