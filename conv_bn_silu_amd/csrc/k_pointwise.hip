@@ -151,17 +151,24 @@ __global__ __launch_bounds__(kThreadsPw, 1) void pointwise_bf16(
     // cache line several times over and costs more than streaming x.)
     const int co = ct * kTileCo + wave * 32 + l32;
     {
+        // Every workgroup reads the same tile at the same moment; each starts
+        // at its own 1 KiB-aligned point of it (a rotation by the block id),
+        // so that the requests spread over L2 channels instead of all
+        // meeting on the same lines (the 1x1 layer at N=8, 256 -> 256, 80x80:
+        // 14.9 -> 14.7 us, same bits).
         constexpr int NW = kTileCo * OCT / kThreadsPw;  // octets per thread
+        constexpr int TOT = kTileCo * OCT;
+        const int rot = (int)(((unsigned)blockIdx.x * 37u) % (unsigned)(TOT / 64)) * 64;
         u32x4 wv[NW];
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            const int t = tid + i * kThreadsPw, r = t / OCT, o = t % OCT;
+            const int t = (tid + i * kThreadsPw + rot) % TOT, r = t / OCT, o = t % OCT;
             const int c = ct * kTileCo + r;
             wv[i] = buf_load16(wr, (c < s.C_out && 8 * o < s.C_in) ? (uint32_t)(c * s.C_in + 8 * o) * 2u : kOOB);
         }
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            const int t = tid + i * kThreadsPw, r = t / OCT, o = t % OCT;
+            const int t = (tid + i * kThreadsPw + rot) % TOT, r = t / OCT, o = t % OCT;
             *(u32x4 *)(wsm + (r * OCT + (o ^ (r & SW))) * 16) = wv[i];
         }
     }
