@@ -73,7 +73,6 @@ __device__ __forceinline__ void rows_for(F &&f) {
     }
 }
 
-
 constexpr int kRowsWaves = 4;                      // consumer waves, and producer waves
 constexpr int kRowsThreads = 2 * 64 * kRowsWaves;  // one consumer and one producer wave per SIMD
 constexpr int kRowsTile = 32 * kRowsWaves;         // output channels per workgroup
@@ -90,6 +89,8 @@ struct RowsGeo {
     static constexpr int OWMAX = 32 * NB;
     static constexpr int P = (NB % 2 == 1) ? 2 * OWMAX : 2 * OWMAX + 64;  // row pitch, odd multiple of 64
     static constexpr int SET = kKRows * P;                                // bytes per set
+    // 16-byte copy tasks per unit: 3 input rows x 16 channels x (2*OWMAX)/8
+    // segments, 63 new ones per wave-wide load, over the producer waves
     static constexpr int TASKS = 3 * kChunk * (2 * OWMAX / 8);
     static constexpr int MAXT = ((TASKS + 62) / 63 + kRowsWaves - 1) / kRowsWaves;
     static constexpr int YP = 2 * OWMAX + 16;                             // y staging pitch (bytes per channel)
@@ -104,6 +105,8 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
     using G = RowsGeo<NB>;
     __shared__ __attribute__((aligned(16))) unsigned char sets[kSets * G::SET];
     __shared__ __attribute__((aligned(16))) unsigned char ystage[G::YSTAGE];
+    // Target of the staging writes of idle producer lanes, so that the writes
+    // need no branch.
     __shared__ __attribute__((aligned(16))) unsigned char sink[2 * G::P + 8];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -136,13 +139,21 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
         // Producer: unit u+1 into set (u+1)%2 after the barrier of unit u
         // (that set was last read in unit u-1), then unit u+1+PD requested
         // into the freed registers, then a share of the previous row's y.
-        constexpr int PD = NCH == 3 ? 3 : (NB == 5 && !W8 && NCH <= 2) ? 2 : kRowsPD;  // a multiple of NCH
+        // Units in flight: a multiple of NCH, so that the unrolled loop knows
+        // each unit's chunk and register slot; two where the 8-byte output
+        // pieces of the widest rows leave fewer registers (the time does not
+        // depend on it between one and six units).
+        constexpr int PD = NCH == 3 ? 3 : (NB == 5 && !W8 && NCH <= 2) ? 2 : kRowsPD;
         const int pw = wave - kRowsWaves;
         const int ptid = tid - 64 * kRowsWaves;
         const int segs = s.W / 8;
         const int tasks = 3 * kChunk * segs;
         const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.C_in * s.H * s.W * 2u);
         const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)s.N * s.C_out * s.OHW * 2u);
+        // Copy task q of this lane: segment t = 63 (4 q + pw) + lane - 1 of
+        // the unit, i.e. input row kh of the unit, channel ci of the chunk,
+        // 8-column segment seg.  Consecutive lanes hold consecutive segments;
+        // lane 0 holds the segment before lane 1's and is only loaded.
         int tk_kh[G::MAXT], tk_lds[G::MAXT];
         uint32_t tk_goff[G::MAXT];
         bool tk_load[G::MAXT], tk_valid[G::MAXT], tk_first[G::MAXT];
