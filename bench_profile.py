@@ -57,7 +57,8 @@ gpurun_out/).
   python3 bench_profile.py dispatch
       bench.py --variants --no-cpu-baseline in a child: every variant that
       supports each of the five workloads and of the dispatch sweep's
-      shapes, timed, against AUTO's pick; writes profiles/dispatch_sweep.md
+      shapes, timed (best of three interleaved rounds), against AUTO's
+      pick; writes profiles/dispatch_sweep.md
       (exits non-zero, as bench.py does, when AUTO is more than 5% slower
       than the fastest variant anywhere).
 

@@ -207,19 +207,32 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
         const int ppr = s.OW / PX;
         const int npieces = kRowsTile * ppr;
         const bool whole = (s.OW & 31) == 0;
+        // A piece's place does not depend on the row: its staging offset and
+        // its offset in y from the row's first element are computed once
+        // (the division by ppr would otherwise cost the producers some thirty
+        // vector instructions per piece, and their instructions are on the
+        // critical path).
+        int pk_src[KMAX];
+        uint32_t pk_y[KMAX];
+        bool pk_ok[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int p = k * 256 + ptid;
+            const int col = p / ppr, pc = p - col * ppr;
+            const int cog = ct * kRowsTile + col;
+            pk_ok[k] = p < npieces && cog < s.C_out;
+            pk_src[k] = (pk_ok[k] ? col : 0) * G::YP + pc * (2 * PX);
+            pk_y[k] = pk_ok[k] ? (uint32_t)(cog * s.OHW + pc * PX) * 2u : 0u;
+        }
         auto store_y = [&](int t, auto partc) __attribute__((always_inline)) {
             constexpr int part = decltype(partc)::value;
             const UnitPos up = unit_pos(t * nchunks);
+            const uint32_t rowbase = (uint32_t)((up.n * s.C_out * s.OH + up.oh) * s.OW) * 2u;
             rows_for<0, KMAX>([&](auto kc) {
                 constexpr int k = decltype(kc)::value;
                 if constexpr (part == NCH || k % NCH == part) {
-                const int p = k * 256 + ptid;
-                const int col = p / ppr, pc = p - col * ppr;
-                const int cog = ct * kRowsTile + col;
-                const bool ok = p < npieces && cog < s.C_out;
-                const unsigned char *src = ystage + (ok ? col : 0) * G::YP + pc * (2 * PX);
-                const uint32_t off = ok ? (uint32_t)(((up.n * s.C_out + cog) * s.OH + up.oh) * s.OW + pc * PX) * 2u
-                                        : kOOB;
+                const unsigned char *src = ystage + pk_src[k];
+                const uint32_t off = pk_ok[k] ? rowbase + pk_y[k] : kOOB;
                 if constexpr (W8) {
                     const u32x4 v = *(const u32x4 *)src;
                     if (whole) buf_store16_nt(yr, off, v);
