@@ -344,7 +344,26 @@ __global__ __launch_bounds__(kRowsThreads, 1) void rows_bf16(
             for (int q = 0; q < 4; ++q) {
                 float o[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = EPI == kFused ? bn_silu(acc[b][4 * q + r], sc, bi) : acc[b][4 * q + r];
+                for (int r = 0; r < 4; ++r) o[r] = acc[b][4 * q + r];
+                if constexpr (EPI == kFused) {
+                    // bn_silu on four values as four interleaved chains (the
+                    // same operations; the scheduling barriers keep the
+                    // compiler, short of registers here, from running them
+                    // one after another, where each waits for its
+                    // transcendentals: 84.7 -> 83.6 us on the stride-2 layer
+                    // at N=16, 64 -> 128, 320x320, same bits).
+                    float e[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = __builtin_fmaf(o[r], sc, bi);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(o[r] * -1.4426950408889634f);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_rcpf(1.0f + e[r]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = o[r] * e[r];
+                }
                 *(u32x2 *)(ydst + 2 * (32 * b + 8 * q)) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
             }
     }
